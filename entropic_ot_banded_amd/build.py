@@ -1,0 +1,54 @@
+"""Build libsinkattn.so (HIP for gfx950) in place, next to this file.
+
+    python -m entropic_ot_banded_amd.build [--debug]
+
+Compiles csrc/*.hip and csrc/api.cpp with hipcc into one shared library.
+Packed fp32 VALU instructions are disabled for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+LIB = os.path.join(HERE, "libsinkattn.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def sources():
+    out = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
+    out.append(os.path.join(CSRC, "api.cpp"))
+    return out
+
+
+def build(debug: bool = False, verbose: bool = False) -> str:
+    """Compile every source into libsinkattn.so; returns the library path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-std=c++17", "-shared", "-fPIC",
+           "-O1" if debug else "-O3", "-I", INCLUDE, "-I", CSRC,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-result", "-x", "hip"] + sources() + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libsinkattn.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(debug="--debug" in sys.argv, verbose=True))

@@ -1,0 +1,141 @@
+// C-ABI of the banded Sinkhorn attention library: argument validation, band
+// geometry, workspace layout and the stream-ordered launch sequence.  Every
+// check here runs on the host before anything is enqueued, so a bad call
+// returns a status code without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/sinkattn.h"
+#include "geom.hpp"
+
+namespace sinkattn {
+
+hipError_t launch_forward(const Geom& g, int dtype, const FwdLaunch& f, const Workspace& w, hipStream_t st);
+hipError_t launch_backward(const Geom& g, int dtype, const BwdLaunch& f, const Workspace& w, hipStream_t st);
+
+namespace {
+
+constexpr int kMaxTailBackward = 8;
+
+bool dtype_d_supported(int dtype, int d) {
+  if (dtype == SINKATTN_F32) return d == 16 || d == 32 || d == 64;
+  if (dtype == SINKATTN_BF16) return d == 32 || d == 64 || d == 128;
+  return false;
+}
+
+// Validate the shape descriptor; fill the band geometry for band width W.
+int make_geom(const sinkattn_shape* s, int W, Geom* g) {
+  if (!s) return SINKATTN_EINVAL;
+  if (s->B < 1 || s->H < 1 || s->L < 1 || s->d < 1) return SINKATTN_EINVAL;
+  if (s->dtype != SINKATTN_F32 && s->dtype != SINKATTN_BF16) return SINKATTN_EINVAL;
+  if (W < 1) return SINKATTN_EINVAL;
+  if (s->dustbin && !s->lengths) return SINKATTN_EINVAL;  // dustbin index n_b needs n_b < L
+  const long long bhl = (long long)s->B * s->H * s->L;
+  if (bhl * s->d > (long long)INT_MAX * 4 || bhl > INT_MAX) return SINKATTN_EUNSUPPORTED;
+  if (!dtype_d_supported(s->dtype, s->d)) return SINKATTN_EUNSUPPORTED;
+  Geom x{};
+  x.B = s->B;
+  x.H = s->H;
+  x.L = s->L;
+  x.d = s->d;
+  int h1 = W / 2, h2 = (W + 1) / 2 - 1;
+  // offsets beyond L - 1 never occur: clamp (keeps W >= 2L - 1 cheap)
+  if (h1 > s->L - 1) h1 = s->L - 1;
+  if (h2 > s->L - 1) h2 = s->L - 1;
+  x.h1 = h1;
+  x.h2 = h2;
+  x.TL = (h1 + 15) / 16;
+  x.TR = (15 + h2) / 16;
+  x.NT = x.TL + x.TR + 1;
+  x.TLc = (h2 + 15) / 16;
+  x.TRc = (15 + h1) / 16;
+  x.NTc = x.TLc + x.TRc + 1;
+  if (x.NT > kMaxTiles || x.NTc > kMaxTiles) return SINKATTN_EUNSUPPORTED;
+  x.nblk = (s->L + kBlockRows - 1) / kBlockRows;
+  x.NWC = 16 * (x.TL + x.TR + kWaves);
+  x.dustbin = s->dustbin ? 1 : 0;
+  x.lengths = s->lengths;
+  x.inv_sqrt_d = 1.0f / std::sqrt((float)s->d);
+  x.scale2 = 1.4426950408889634f * x.inv_sqrt_d;
+  *g = x;
+  return SINKATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace sinkattn
+
+using namespace sinkattn;
+
+extern "C" {
+
+int sinkattn_version(void) { return 10000; }
+
+const char* sinkattn_status_string(int status) {
+  switch (status) {
+    case SINKATTN_OK: return "ok";
+    case SINKATTN_EINVAL: return "invalid argument";
+    case SINKATTN_EUNSUPPORTED: return "unsupported configuration (outside the built kernels' envelope)";
+    case SINKATTN_EHIP: return "HIP runtime or launch error";
+    case SINKATTN_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+size_t sinkattn_workspace_bytes(const sinkattn_shape* s, int W, int R) {
+  Geom g;
+  if (R < 0 || make_geom(s, W, &g) != SINKATTN_OK) return 0;
+  return carve(nullptr, g, R).floats * sizeof(float);
+}
+
+size_t sinkattn_tail_offset(const sinkattn_shape* s, int R, int r, int is_v) {
+  if (!s || R < 0 || r < 0 || r > R || s->B < 1 || s->H < 1 || s->L < 1) return (size_t)-1;
+  const size_t BHL = (size_t)s->B * s->H * s->L;
+  const size_t u_block = align64(2 * (size_t)(R + 1) * BHL) * sizeof(float);  // fp64 slots
+  return (is_v ? u_block : 0) + (size_t)r * BHL * sizeof(double);
+}
+
+int sinkattn_forward(const void* Q, const void* K, const void* V, int W, int T, int R, const float* a,
+                     const float* b, const sinkattn_shape* s, float* O, float* u, float* v, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!Q || !K || !V || !a || !b || !O || !u || !v || !workspace) return SINKATTN_EINVAL;
+  if (T < 0 || R < 0) return SINKATTN_EINVAL;
+  Geom g;
+  int st = make_geom(s, W, &g);
+  if (st != SINKATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+    return SINKATTN_EINVAL;
+  Workspace w = carve(static_cast<float*>(workspace), g, R);
+  if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
+  FwdLaunch f{Q, K, V, a, b, O, u, v, T, R};
+  hipError_t e = launch_forward(g, s->dtype, f, w, stream);
+  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
+  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+}
+
+int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T, int R, const float* a,
+                      const float* b, const sinkattn_shape* s, const float* O, const void* dO, void* workspace,
+                      size_t workspace_bytes, float* dQ, float* dK, float* dV, float* vbar0,
+                      hipStream_t stream) {
+  if (!Q || !K || !V || !a || !b || !O || !dO || !workspace || !dQ || !dK || !dV) return SINKATTN_EINVAL;
+  if (T < 0 || R < 0) return SINKATTN_EINVAL;
+  if (R > kMaxTailBackward) return SINKATTN_EUNSUPPORTED;
+  Geom g;
+  int st = make_geom(s, W, &g);
+  if (st != SINKATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) ||
+      !aligned16(dV) || !aligned16(workspace))
+    return SINKATTN_EINVAL;
+  Workspace w = carve(static_cast<float*>(workspace), g, R);
+  if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
+  BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, vbar0, T, R};
+  hipError_t e = launch_backward(g, s->dtype, f, w, stream);
+  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
+  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,860 @@
+// Backward pass: exact adjoint of the R differentiable tail steps of banded
+// Sinkhorn attention, with the stopped base held constant.
+//
+// "Blockwise Differentiable Sinkhorn Attention", section 2.2: the adjoint of
+// the tail touches the staircase plans P^(r,r) (column updates) and
+// P^(r,r-1) (row updates).  They all lie in one row/column scaling orbit of
+// the reference plan P = P^(R,R):
+//     P^(r,s) = P (.) alpha^(r) beta^(s)^T,
+//     alpha^(r) = exp(u^(r) - u^(R)),  beta^(s) = exp(v^(s) - v^(R)),
+// so every sweep below rebuilds only the reference tile
+// P_ij = exp(S_ij + u^(R)_i + v^(R)_j) (S recomputed on MFMA) and applies
+// O(L) vector modifiers.  With x^(r) = ubar^(r) / a and y^(r) = vbar^(r) / b:
+//   vbar^(R) = E,                E_j = V_j . dV_j,  dV = P^T dO
+//   ubar^(r) = [r = R] D - alpha^(r) (.) P (beta^(r) (.) y^(r)),  D_i = dO_i . O_i
+//   vbar^(r-1) = -beta^(r-1) (.) P^T (alpha^(r) (.) x^(r))
+//   dS = P (.) (dO V^T - sum_r [alpha^(r) (beta^(r) y^(r))^T + (alpha^(r) x^(r)) beta^(r-1)^T])
+//   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
+// Sweeps: one column sweep (dV), R row sweeps and R column sweeps for the
+// adjoint vectors (the last column sweep only when vbar^(0) is requested),
+// a row sweep for dQ and a column sweep for dK.  All accumulations run in a
+// fixed order inside one workgroup: results are bitwise reproducible.
+//
+// Units: the tail stack holds potentials in log2 units (x * log2(e)) and
+// scores are taken as S * log2(e) / sqrt(d), so every plan entry and
+// modifier is one exp2 of a sum; gradients come out in natural units.
+//
+// Row sweeps put one query row per lane (score tile = K_tile Q_strip^T);
+// column sweeps put one key column per lane (score tile = Q_tile K_strip^T).
+// The second operand of the output products (K for dQ, Q for dK, dO for dV)
+// is staged transposed in LDS.  bf16: P and dS are split into hi + lo bf16
+// operands (~16 mantissa bits).
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "geom.hpp"
+
+namespace sinkattn {
+
+constexpr int kMaxR = 8;
+
+struct BwArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const float* O;
+  const float* a;
+  const float* b;
+  const double* tail_u;  // [R+1][BHL] (fp64, log2 units)
+  const double* tail_v;  // [R+1][BHL]
+  const float* sdr;
+  const float* sdc;
+  float* D;             // [BHL]
+  float* vbar;          // [R+1][BHL]
+  float* x;             // [R+1][BHL]
+  float* out;           // dQ / dK / dV
+  int R;
+  int r;                // pass index (vector sweeps)
+  int padded_grid;
+};
+
+__device__ __forceinline__ size_t slot(int r, size_t BHL) { return (size_t)r * BHL; }
+
+// Tile-pair product: acc[dc] += A^T-operand tile pair (C layout, lane = m
+// index) times rows of a transposed LDS window (element stride `stride`).
+// k slot 8*lg + e maps to window column c0 + e (e < 4) / c0 + 12 + e (e >= 4).
+template <typename T, int ND>
+__device__ __forceinline__ void acc_pair(f4 (&acc)[ND], const float (&p0)[4], const float (&p1)[4],
+                                         bool has1, const char* tw, int stride, int c0, int lr) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hb[r] = float_to_bf16_bits(p0[r]);
+      hb[4 + r] = float_to_bf16_bits(p1[r]);
+      lb[r] = float_to_bf16_bits(p0[r] - bits_to_float(hb[r] << 16));
+      lb[4 + r] = float_to_bf16_bits(p1[r] - bits_to_float(hb[4 + r] << 16));
+    }
+    const u4 hi = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+    const u4 lo = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) {
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(tw) + (size_t)(dc * 16 + lr) * stride;
+      const u2 x0 = *reinterpret_cast<const u2*>(row + c0);
+      u2 x1 = {0u, 0u};
+      if (has1) x1 = *reinterpret_cast<const u2*>(row + c0 + 16);
+      const u4 vb = {x0.x, x0.y, x1.x, x1.y};
+      acc[dc] = Elt<bf16_t>::mma_chunk(acc[dc], hi, vb);
+      acc[dc] = Elt<bf16_t>::mma_chunk(acc[dc], lo, vb);
+    }
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) {
+      const float* row = reinterpret_cast<const float*>(tw) + (size_t)(dc * 16 + lr) * stride;
+      const f4 v0 = *reinterpret_cast<const f4*>(row + c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dc] = __builtin_amdgcn_mfma_f32_16x16x4f32(p0[r], v0[r], acc[dc], 0, 0, 0);
+      if (has1) {
+        const f4 v1 = *reinterpret_cast<const f4*>(row + c0 + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dc] = __builtin_amdgcn_mfma_f32_16x16x4f32(p1[r], v1[r], acc[dc], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Stage rows [row0, row0 + nrows) of a [L, D] tensor (zero outside [0, n))
+// into LDS transposed: dst[c * stride + k] = X[row0 + k][c].
+template <typename T, int D>
+__device__ __forceinline__ void stage_transposed(char* dst, int stride, const void* Xbh, int row0, int nrows, int n,
+                                                 int tid, int nthreads) {
+  constexpr int RB = D * Elt<T>::kBytes;
+  constexpr int per_row = RB / 16;
+  const char* X = reinterpret_cast<const char*>(Xbh);
+  for (int idx = tid; idx < nrows * per_row; idx += nthreads) {
+    const int k = idx / per_row, c16 = idx - k * per_row;
+    const int row = row0 + k;
+    u4 val = {0u, 0u, 0u, 0u};
+    if (row >= 0 && row < n) val = ld16(X + (size_t)row * RB + c16 * 16);
+    if constexpr (sizeof(T) == 2) {
+      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) reinterpret_cast<uint16_t*>(dst)[(size_t)(c16 * 8 + e) * stride + k] = hv[e];
+    } else {
+      const uint32_t* fv = reinterpret_cast<const uint32_t*>(&val);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) reinterpret_cast<uint32_t*>(dst)[(size_t)(c16 * 4 + e) * stride + k] = fv[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row sweeps.  MODE 0: adjoint vector pass r (writes x^(r)); MODE 1: dQ.
+// Block = 4 strips of 16 rows; window columns [r0 - 16 TL, r0 + 64 + 16 TR).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) void bw_row_kernel(Geom g, BwArgs p) {
+  constexpr int RB = D * Elt<T>::kBytes;
+  constexpr int NCH = RB / 64;
+  constexpr int ND = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nbh = g.B * g.H;
+  const int nblk = ceil_div_pos(g.L, kBwdBlock);
+  const int logical = xcd_remap(blockIdx.x, p.padded_grid);
+  if (logical >= nbh * nblk) return;
+  const int bh = logical / nblk;
+  const int blk = logical - bh * nblk;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const int r0 = blk * kBwdBlock;
+  if (r0 >= n) return;
+  const size_t L = g.L;
+  const size_t BHL = (size_t)nbh * L;
+  const int R = p.R;
+  const int NWC = 16 * (g.TL + g.TR + kBwdWaves);
+  const int tw0 = (r0 >> 4) - g.TL;
+  const int tid = threadIdx.x;
+  const int KTS = NWC + 8;  // transposed-K row stride (elements)
+
+  // LDS: w [NWC] | colvec [2R or 1][NWC] | K^T [D][KTS]
+  float* w2s = reinterpret_cast<float*>(smem);
+  float* cv = w2s + NWC;
+  const int ncv = MODE == 0 ? 1 : 2 * R;
+  char* kt = reinterpret_cast<char*>(cv + (size_t)(ncv > 0 ? ncv : 1) * NWC);
+  const double* vR = p.tail_v + slot(R, BHL) + bh * L;
+  const double* uR = p.tail_u + slot(R, BHL) + bh * L;
+  const double vref = vR[r0];  // exponents split as (u_i + vref) + (v_j - vref)
+  for (int c = tid; c < NWC; c += blockDim.x) {
+    const int j = tw0 * 16 + c;
+    const bool ok = j >= 0 && j < n;
+    w2s[c] = ok ? (float)(vR[j] - vref) : kNegInf;
+    if (MODE == 0) {
+      // z_j = beta^(r)_j y^(r)_j
+      float z = 0.f;
+      if (ok) {
+        const double vr = p.tail_v[slot(p.r, BHL) + bh * L + j];
+        z = exp2f(vr - vR[j]) * p.vbar[slot(p.r, BHL) + bh * L + j] / p.b[(size_t)bb * L + j];
+      }
+      cv[c] = z;
+    } else {
+      for (int k = 1; k <= R; ++k) {
+        float by = 0.f, bm = 0.f;
+        if (ok) {
+          const double vk = p.tail_v[slot(k, BHL) + bh * L + j];
+          const double vk1 = p.tail_v[slot(k - 1, BHL) + bh * L + j];
+          by = exp2f(vk - vR[j]) * p.vbar[slot(k, BHL) + bh * L + j] / p.b[(size_t)bb * L + j];
+          bm = exp2f(vk1 - vR[j]);
+        }
+        cv[(size_t)(2 * (k - 1)) * NWC + c] = by;
+        cv[(size_t)(2 * (k - 1) + 1) * NWC + c] = bm;
+      }
+    }
+  }
+  if (MODE == 1) {
+    stage_transposed<T, D>(kt, KTS, reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB, tw0 * 16, NWC, n,
+                           tid, blockDim.x);
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int i0 = r0 + wave * 16;
+  if (i0 >= n) return;
+  const int NT = g.NT;
+  const int tg0 = tw0 + wave;
+  int t_lo = -tg0;
+  t_lo = t_lo < 0 ? 0 : t_lo;
+  int t_hi = (n - 1) / 16 - tg0;
+  t_hi = t_hi > NT - 1 ? NT - 1 : t_hi;
+
+  const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
+  const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
+  const char* Vb = reinterpret_cast<const char*>(p.V) + (size_t)bh * L * RB;
+  const char* dOb = reinterpret_cast<const char*>(p.dO) + (size_t)bh * L * RB;
+  const int qi = i0 + lr;
+  const bool myrow = qi < n;
+  u4 qb[NCH], ob[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    qb[c] = (u4){0u, 0u, 0u, 0u};
+    ob[c] = (u4){0u, 0u, 0u, 0u};
+    if (myrow) {
+      qb[c] = ld16(Qb + (size_t)qi * RB + c * 64 + lg * 16);
+      if (MODE == 1) ob[c] = ld16(dOb + (size_t)qi * RB + c * 64 + lg * 16);
+    }
+  }
+  const float ui2 = myrow ? (float)(uR[qi] + vref) : 0.f;
+  // row modifiers (MODE 1): alpha^(k)_i, alpha^(k)_i x^(k)_i
+  float al[kMaxR], ax[kMaxR];
+#pragma unroll
+  for (int k = 0; k < kMaxR; ++k) {
+    al[k] = 0.f;
+    ax[k] = 0.f;
+    if (MODE == 1 && k < R && myrow) {
+      al[k] = exp2f(p.tail_u[slot(k + 1, BHL) + bh * L + qi] - uR[qi]);
+      ax[k] = al[k] * p.x[slot(k + 1, BHL) + bh * L + qi];
+    }
+  }
+
+  auto tile = [&](int t, float (&pt)[4], float (&dst)[4]) {
+    if (t >= NT || t < t_lo || t > t_hi) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { pt[r] = 0.f; dst[r] = 0.f; }
+      return;
+    }
+    const int jrow = (tg0 + t) * 16 + lr;
+    const bool kin = jrow >= 0 && jrow < n;
+    f4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      u4 ka = {0u, 0u, 0u, 0u}, va = {0u, 0u, 0u, 0u};
+      if (kin) {
+        ka = ld16(Kb + (size_t)jrow * RB + c * 64 + lg * 16);
+        if (MODE == 1) va = ld16(Vb + (size_t)jrow * RB + c * 64 + lg * 16);
+      }
+      s = Elt<T>::mma_chunk(s, ka, qb[c]);
+      if (MODE == 1) dp = Elt<T>::mma_chunk(dp, va, ob[c]);
+    }
+    const int obase = (t - g.TL) * 16 + 4 * lg - lr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = obase + r;
+      const int c = (wave + t) * 16 + 4 * lg + r;
+      float x = __builtin_fmaf(s[r], g.scale2, w2s[c] + ui2);
+      x = (o >= -g.h1 && o <= g.h2 && myrow) ? x : kNegInf;
+      pt[r] = exp2_fast(x);
+      if (MODE == 1) {
+        float br = dp[r];
+#pragma unroll
+        for (int k = 0; k < kMaxR; ++k) {
+          if (k < R) {
+            br -= al[k] * cv[(size_t)(2 * k) * NWC + c];
+            br -= ax[k] * cv[(size_t)(2 * k + 1) * NWC + c];
+          }
+        }
+        dst[r] = pt[r] * br;
+      } else {
+        dst[r] = pt[r] * cv[c];
+      }
+    }
+  };
+
+  if (MODE == 0) {
+    float acc = 0.f;
+    for (int t = 0; t < NT; ++t) {
+      float pt[4], pz[4];
+      tile(t, pt, pz);
+      acc += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+    }
+    acc = cross_row_sum(acc);
+    if (lg == 0 && myrow) {
+      const int i = qi;
+      if (g.dustbin) {
+        // entry (i, delta): P_i,delta z_delta
+        const double vRd = p.tail_v[slot(R, BHL) + bh * L + n];
+        const float zd = exp2f(p.tail_v[slot(p.r, BHL) + bh * L + n] - vRd) *
+                         p.vbar[slot(p.r, BHL) + bh * L + n] / p.b[(size_t)bb * L + n];
+        acc += exp2f(p.sdc[bh * L + i] + uR[i] + vRd) * zd;
+      }
+      const float alpha = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + i] - uR[i]);
+      const float ub = (p.r == R ? p.D[bh * L + i] : 0.f) - alpha * acc;
+      p.x[slot(p.r, BHL) + bh * L + i] = ub / p.a[(size_t)bb * L + i];
+    }
+  } else {
+    f4 acc[ND];
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) acc[dc] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; t += 2) {
+      float p0[4], s0[4], p1[4], s1[4];
+      tile(t, p0, s0);
+      tile(t + 1, p1, s1);
+      const int c0 = (wave + t) * 16 + 4 * lg;
+      acc_pair<T, ND>(acc, s0, s1, t + 1 < NT, kt, KTS, c0, lr);
+    }
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * lg + r;
+        if (i < n) p.out[((size_t)bh * L + i) * D + dc * 16 + lr] = acc[dc][r] * g.inv_sqrt_d;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column sweeps.  MODE 0: adjoint vector pass (writes vbar^(r-1));
+// MODE 1: dK; MODE 2: dV (band part).
+// Block = 4 strips of 16 columns; window rows [c0 - 16 TLc, c0 + 64 + 16 TRc).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) void bw_col_kernel(Geom g, BwArgs p) {
+  constexpr int RB = D * Elt<T>::kBytes;
+  constexpr int NCH = RB / 64;
+  constexpr int ND = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nbh = g.B * g.H;
+  const int nblk = ceil_div_pos(g.L, kBwdBlock);
+  const int logical = xcd_remap(blockIdx.x, p.padded_grid);
+  if (logical >= nbh * nblk) return;
+  const int bh = logical / nblk;
+  const int blk = logical - bh * nblk;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const int c0b = blk * kBwdBlock;
+  if (c0b >= n) return;
+  const size_t L = g.L;
+  const size_t BHL = (size_t)nbh * L;
+  const int R = p.R;
+  const int NWR = 16 * (g.TLc + g.TRc + kBwdWaves);
+  const int tw0 = (c0b >> 4) - g.TLc;
+  const int tid = threadIdx.x;
+  const int XTS = NWR + 8;
+
+  float* w2s = reinterpret_cast<float*>(smem);   // u^(R) (log2) of window rows
+  float* rv = w2s + NWR;                         // row vectors
+  const int nrv = MODE == 0 ? 1 : (MODE == 1 ? 2 * R : 0);
+  char* xt = reinterpret_cast<char*>(rv + (size_t)(nrv > 0 ? nrv : 1) * NWR);
+  const double* vR = p.tail_v + slot(R, BHL) + bh * L;
+  const double* uR = p.tail_u + slot(R, BHL) + bh * L;
+  const double uref = uR[c0b];  // exponents split as (u_i - uref) + (v_j + uref)
+  for (int c = tid; c < NWR; c += blockDim.x) {
+    const int i = tw0 * 16 + c;
+    const bool ok = i >= 0 && i < n;
+    w2s[c] = ok ? (float)(uR[i] - uref) : kNegInf;
+    if (MODE == 0) {
+      // zz_i = alpha^(r)_i x^(r)_i
+      float z = 0.f;
+      if (ok) z = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + i] - uR[i]) * p.x[slot(p.r, BHL) + bh * L + i];
+      rv[c] = z;
+    } else if (MODE == 1) {
+      for (int k = 1; k <= R; ++k) {
+        float al = 0.f, ax = 0.f;
+        if (ok) {
+          al = exp2f(p.tail_u[slot(k, BHL) + bh * L + i] - uR[i]);
+          ax = al * p.x[slot(k, BHL) + bh * L + i];
+        }
+        rv[(size_t)(2 * (k - 1)) * NWR + c] = al;
+        rv[(size_t)(2 * (k - 1) + 1) * NWR + c] = ax;
+      }
+    }
+  }
+  if (MODE == 1)
+    stage_transposed<T, D>(xt, XTS, reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB, tw0 * 16, NWR, n, tid,
+                           blockDim.x);
+  if (MODE == 2)
+    stage_transposed<T, D>(xt, XTS, reinterpret_cast<const char*>(p.dO) + (size_t)bh * L * RB, tw0 * 16, NWR, n, tid,
+                           blockDim.x);
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int j0 = c0b + wave * 16;
+  if (j0 >= n) return;
+  const int NT = g.NTc;
+  const int tg0 = tw0 + wave;
+  int t_lo = -tg0;
+  t_lo = t_lo < 0 ? 0 : t_lo;
+  int t_hi = (n - 1) / 16 - tg0;
+  t_hi = t_hi > NT - 1 ? NT - 1 : t_hi;
+
+  const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
+  const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
+  const char* Vb = reinterpret_cast<const char*>(p.V) + (size_t)bh * L * RB;
+  const char* dOb = reinterpret_cast<const char*>(p.dO) + (size_t)bh * L * RB;
+  const int kj = j0 + lr;
+  const bool mycol = kj < n;
+  u4 kb[NCH], vb[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    kb[c] = (u4){0u, 0u, 0u, 0u};
+    vb[c] = (u4){0u, 0u, 0u, 0u};
+    if (mycol) {
+      kb[c] = ld16(Kb + (size_t)kj * RB + c * 64 + lg * 16);
+      if (MODE == 1) vb[c] = ld16(Vb + (size_t)kj * RB + c * 64 + lg * 16);
+    }
+  }
+  const float vj2 = mycol ? (float)(vR[kj] + uref) : 0.f;
+  // column modifiers (MODE 1): beta^(k)_j y^(k)_j and beta^(k-1)_j
+  float by[kMaxR], bm[kMaxR];
+#pragma unroll
+  for (int k = 0; k < kMaxR; ++k) {
+    by[k] = 0.f;
+    bm[k] = 0.f;
+    if (MODE == 1 && k < R && mycol) {
+      by[k] = exp2f(p.tail_v[slot(k + 1, BHL) + bh * L + kj] - vR[kj]) * p.vbar[slot(k + 1, BHL) + bh * L + kj] /
+              p.b[(size_t)bb * L + kj];
+      bm[k] = exp2f(p.tail_v[slot(k, BHL) + bh * L + kj] - vR[kj]);
+    }
+  }
+
+  auto tile = [&](int t, float (&pt)[4], float (&dst)[4]) {
+    if (t >= NT || t < t_lo || t > t_hi) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { pt[r] = 0.f; dst[r] = 0.f; }
+      return;
+    }
+    const int irow = (tg0 + t) * 16 + lr;
+    const bool qin = irow >= 0 && irow < n;
+    f4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      u4 qa = {0u, 0u, 0u, 0u}, oa = {0u, 0u, 0u, 0u};
+      if (qin) {
+        qa = ld16(Qb + (size_t)irow * RB + c * 64 + lg * 16);
+        if (MODE == 1) oa = ld16(dOb + (size_t)irow * RB + c * 64 + lg * 16);
+      }
+      s = Elt<T>::mma_chunk(s, qa, kb[c]);
+      if (MODE == 1) dp = Elt<T>::mma_chunk(dp, oa, vb[c]);
+    }
+    // lane: i = (tg0 + t) * 16 + 4 lg + r, j = j0 + lr
+    const int obase = (g.TLc - t) * 16 + lr - 4 * lg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = obase - r;
+      const int c = (wave + t) * 16 + 4 * lg + r;
+      float x = __builtin_fmaf(s[r], g.scale2, w2s[c] + vj2);
+      x = (o >= -g.h1 && o <= g.h2 && mycol) ? x : kNegInf;
+      pt[r] = exp2_fast(x);
+      if (MODE == 1) {
+        float br = dp[r];
+#pragma unroll
+        for (int k = 0; k < kMaxR; ++k) {
+          if (k < R) {
+            br -= rv[(size_t)(2 * k) * NWR + c] * by[k];
+            br -= rv[(size_t)(2 * k + 1) * NWR + c] * bm[k];
+          }
+        }
+        dst[r] = pt[r] * br;
+      } else if (MODE == 0) {
+        dst[r] = pt[r] * rv[c];
+      } else {
+        dst[r] = pt[r];
+      }
+    }
+  };
+
+  if (MODE == 0) {
+    float acc = 0.f;
+    for (int t = 0; t < NT; ++t) {
+      float pt[4], pz[4];
+      tile(t, pt, pz);
+      acc += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+    }
+    acc = cross_row_sum(acc);
+    if (lg == 0 && mycol) {
+      const int j = kj;
+      if (g.dustbin) {
+        // entry (delta, j): P_delta,j zz_delta
+        const double uRd = p.tail_u[slot(R, BHL) + bh * L + n];
+        const float zd = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + n] - uRd) * p.x[slot(p.r, BHL) + bh * L + n];
+        acc += exp2f(p.sdr[bh * L + j] + uRd + vR[j]) * zd;
+      }
+      const float beta = exp2f(p.tail_v[slot(p.r - 1, BHL) + bh * L + j] - vR[j]);
+      p.vbar[slot(p.r - 1, BHL) + bh * L + j] = -beta * acc;
+    }
+  } else {
+    f4 acc[ND];
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) acc[dc] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; t += 2) {
+      float p0[4], s0[4], p1[4], s1[4];
+      tile(t, p0, s0);
+      tile(t + 1, p1, s1);
+      const int c0 = (wave + t) * 16 + 4 * lg;
+      acc_pair<T, ND>(acc, s0, s1, t + 1 < NT, xt, XTS, c0, lr);
+    }
+    const float sc = MODE == 1 ? g.inv_sqrt_d : 1.f;
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + 4 * lg + r;
+        if (j < n) p.out[((size_t)bh * L + j) * D + dc * 16 + lr] = acc[dc][r] * sc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token kernels (one thread per token, d-long loops).
+// ---------------------------------------------------------------------------
+// D_i = dO_i . O_i on active rows.
+template <typename T>
+__global__ void bw_rowdot(Geom g, const T* dO, const float* O, float* Dv) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.L) return;
+  const int n = real_len(g, bh / g.H);
+  const int nact = n + (g.dustbin ? 1 : 0);
+  const size_t o = (size_t)bh * g.L + i;
+  float s = 0.f;
+  if (i < nact)
+    for (int c = 0; c < g.d; ++c) s = __builtin_fmaf(Elt<T>::load(dO, o * g.d + c), O[o * g.d + c], s);
+  Dv[o] = s;
+}
+
+// After the dV sweep: add the dustbin-row entry (delta, j) for real j, zero
+// filler rows, E_j = V_j . dV_j, vbar^(R)_j = E_j.
+template <typename T>
+__global__ void bw_finish_dv(Geom g, const T* V, const T* dO, const double* tail_u, const double* tail_v,
+                             const float* sdr, int R, float* dV, float* vbarR) {
+  const int bh = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= g.L) return;
+  const int n = real_len(g, bh / g.H);
+  const size_t L = g.L;
+  const size_t BHL = (size_t)g.B * g.H * L;
+  const size_t o = (size_t)bh * L + j;
+  const int d = g.d;
+  if (j >= n) {
+    if (!(g.dustbin && j == n)) {
+      for (int c = 0; c < d; ++c) dV[o * d + c] = 0.f;
+      vbarR[o] = 0.f;
+    }
+    return;
+  }
+  float pdj = 0.f;
+  if (g.dustbin) {
+    const double uRd = tail_u[slot(R, BHL) + bh * L + n];
+    pdj = exp2f(sdr[o] + uRd + tail_v[slot(R, BHL) + o]);
+  }
+  const size_t od = (size_t)bh * L + n;
+  float e = 0.f;
+  for (int c = 0; c < d; ++c) {
+    float dv = dV[o * d + c];
+    if (g.dustbin) dv = __builtin_fmaf(pdj, Elt<T>::load(dO, od * d + c), dv);
+    dV[o * d + c] = dv;
+    e = __builtin_fmaf(Elt<T>::load(V, o * d + c), dv, e);
+  }
+  vbarR[o] = e;
+}
+
+// After the dQ (IS_K = 0) or dK (IS_K = 1) sweep: add the dustbin entry of
+// every real token and zero filler rows.
+//   dQ_i += dS_i,delta K_delta / sqrt(d);  dK_j += dS_delta,j Q_delta / sqrt(d)
+template <typename T, int IS_K>
+__global__ void bw_finish_grad(Geom g, BwArgs p) {
+  const int bh = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= g.L) return;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const size_t L = g.L;
+  const size_t BHL = (size_t)g.B * g.H * L;
+  const int d = g.d;
+  const int R = p.R;
+  const size_t o = (size_t)bh * L + t;
+  if (t >= n) {
+    if (!(g.dustbin && t == n))
+      for (int c = 0; c < d; ++c) p.out[o * d + c] = 0.f;
+    return;
+  }
+  if (!g.dustbin) return;
+  const T* Q = reinterpret_cast<const T*>(p.Q);
+  const T* K = reinterpret_cast<const T*>(p.K);
+  const T* V = reinterpret_cast<const T*>(p.V);
+  const T* dO = reinterpret_cast<const T*>(p.dO);
+  const size_t od = (size_t)bh * L + n;
+  const double* uR = p.tail_u + slot(R, BHL);
+  const double* vR = p.tail_v + slot(R, BHL);
+  // the entry: row i, column j
+  const size_t oi = IS_K ? od : o;
+  const size_t oj = IS_K ? o : od;
+  const float s = IS_K ? p.sdr[o] : p.sdc[o];
+  const float P = exp2f(s + uR[oi] + vR[oj]);
+  float dP = 0.f;
+  for (int c = 0; c < d; ++c) dP = __builtin_fmaf(Elt<T>::load(dO, oi * d + c), Elt<T>::load(V, oj * d + c), dP);
+  const int bi = IS_K ? n : t, bj = IS_K ? t : n;
+  float br = dP;
+  for (int k = 1; k <= R; ++k) {
+    const float al = exp2f(p.tail_u[slot(k, BHL) + oi] - uR[oi]);
+    const float x = p.x[slot(k, BHL) + oi];
+    const float by = exp2f(p.tail_v[slot(k, BHL) + oj] - vR[oj]) * p.vbar[slot(k, BHL) + oj] / p.b[(size_t)bb * L + bj];
+    const float bm = exp2f(p.tail_v[slot(k - 1, BHL) + oj] - vR[oj]);
+    br -= al * by + al * x * bm;
+  }
+  (void)bi;
+  const float dS = P * br * g.inv_sqrt_d;
+  const T* X = IS_K ? Q : K;  // the other side's dustbin vector
+  const size_t ox = IS_K ? oi : oj;
+  for (int c = 0; c < d; ++c) p.out[o * d + c] = __builtin_fmaf(dS, Elt<T>::load(X, ox * d + c), p.out[o * d + c]);
+}
+
+// Dustbin row and column (full length), one workgroup per (b, h).
+//   mode 0: dV_delta = sum_i P_i,delta dO_i, vbar^(R)_delta = V_delta . dV_delta
+//   mode 1: x^(r)_delta (row pass r)
+//   mode 2: vbar^(r-1)_delta (column pass r)
+//   mode 3: dQ_delta (row),  mode 4: dK_delta (column)
+template <typename T>
+__global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
+  const int bh = blockIdx.x;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const size_t L = g.L;
+  const size_t BHL = (size_t)g.B * g.H * L;
+  const int d = g.d;
+  const int R = p.R;
+  const int tid = threadIdx.x;
+  const size_t od = (size_t)bh * L + n;
+  const double* uR = p.tail_u + slot(R, BHL);
+  const double* vR = p.tail_v + slot(R, BHL);
+  const T* Q = reinterpret_cast<const T*>(p.Q);
+  const T* K = reinterpret_cast<const T*>(p.K);
+  const T* V = reinterpret_cast<const T*>(p.V);
+  const T* dO = reinterpret_cast<const T*>(p.dO);
+  __shared__ float red[256];
+  // plan entry with the dustbin: row side (delta, t) when row = true
+  auto plan = [&](int t, bool row) {
+    const size_t ot = (size_t)bh * L + t;
+    const float s = row ? p.sdr[ot] : p.sdc[ot];
+    return row ? exp2f(s + uR[od] + vR[ot]) : exp2f(s + uR[ot] + vR[od]);
+  };
+  auto block_sum = [&](float v) {
+    red[tid] = v;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+  };
+  if (mode == 1 || mode == 2) {
+    const int r = p.r;
+    float acc = 0.f;
+    for (int t = tid; t <= n; t += blockDim.x) {
+      const size_t ot = (size_t)bh * L + t;
+      if (mode == 1) {
+        // z_t = beta^(r)_t y^(r)_t over the dustbin row
+        const float z = exp2f(p.tail_v[slot(r, BHL) + ot] - vR[ot]) * p.vbar[slot(r, BHL) + ot] / p.b[(size_t)bb * L + t];
+        acc += plan(t, true) * z;
+      } else {
+        const float z = exp2f(p.tail_u[slot(r, BHL) + ot] - uR[ot]) * p.x[slot(r, BHL) + ot];
+        acc += plan(t, false) * z;
+      }
+    }
+    acc = block_sum(acc);
+    if (tid == 0) {
+      if (mode == 1) {
+        const float alpha = exp2f(p.tail_u[slot(r, BHL) + od] - uR[od]);
+        const float ub = (r == R ? p.D[od] : 0.f) - alpha * acc;
+        p.x[slot(r, BHL) + od] = ub / p.a[(size_t)bb * L + n];
+      } else {
+        const float beta = exp2f(p.tail_v[slot(r - 1, BHL) + od] - vR[od]);
+        p.vbar[slot(r - 1, BHL) + od] = -beta * acc;
+      }
+    }
+    return;
+  }
+  // vector outputs: thread c owns column c of the head dimension
+  for (int c = tid; c < d; c += blockDim.x) {
+    float acc = 0.f;
+    for (int t = 0; t <= n; ++t) {
+      const size_t ot = (size_t)bh * L + t;
+      if (mode == 0) {
+        acc = __builtin_fmaf(plan(t, false), Elt<T>::load(dO, ot * d + c), acc);
+      } else {
+        const bool row = mode == 3;
+        const size_t oi = row ? od : ot, oj = row ? ot : od;
+        const int bj = row ? t : n;
+        const float P = plan(t, row);
+        float dP = 0.f;
+        for (int cc = 0; cc < d; ++cc) dP = __builtin_fmaf(Elt<T>::load(dO, oi * d + cc), Elt<T>::load(V, oj * d + cc), dP);
+        float br = dP;
+        for (int k = 1; k <= R; ++k) {
+          const float al = exp2f(p.tail_u[slot(k, BHL) + oi] - uR[oi]);
+          const float x = p.x[slot(k, BHL) + oi];
+          const float by = exp2f(p.tail_v[slot(k, BHL) + oj] - vR[oj]) * p.vbar[slot(k, BHL) + oj] / p.b[(size_t)bb * L + bj];
+          const float bm = exp2f(p.tail_v[slot(k - 1, BHL) + oj] - vR[oj]);
+          br -= al * by + al * x * bm;
+        }
+        const T* X = row ? K : Q;
+        acc = __builtin_fmaf(P * br, Elt<T>::load(X, ot * d + c), acc);
+      }
+    }
+    if (mode == 0) {
+      p.out[od * d + c] = acc;
+    } else {
+      p.out[od * d + c] = acc * g.inv_sqrt_d;
+    }
+  }
+  if (mode == 0) {
+    __syncthreads();
+    float e = 0.f;
+    for (int c = tid; c < d; c += blockDim.x) e = __builtin_fmaf(Elt<T>::load(V, od * d + c), p.out[od * d + c], e);
+    e = block_sum(e);
+    if (tid == 0) p.vbar[slot(R, BHL) + od] = e;
+  }
+}
+
+// vbar^(0) -> caller buffer (filler = 0).
+__global__ void bw_copy_vbar0(Geom g, const float* vbar0, float* out) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.L) return;
+  const int n = real_len(g, bh / g.H);
+  const int nact = n + (g.dustbin ? 1 : 0);
+  const size_t o = (size_t)bh * g.L + i;
+  out[o] = i < nact ? vbar0[o] : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void dustbin_scores_bw(Geom g, const T* Q, const T* K, float* sdr, float* sdc) {
+  const int bh = blockIdx.y;
+  const int n = real_len(g, bh / g.H);
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j > n) return;
+  const size_t L = g.L;
+  const int d = g.d;
+  float sr = 0.f, sc = 0.f;
+  for (int c = 0; c < d; ++c) {
+    sr = __builtin_fmaf(Elt<T>::load(Q, ((size_t)bh * L + n) * d + c), Elt<T>::load(K, ((size_t)bh * L + j) * d + c), sr);
+    sc = __builtin_fmaf(Elt<T>::load(Q, ((size_t)bh * L + j) * d + c), Elt<T>::load(K, ((size_t)bh * L + n) * d + c), sc);
+  }
+  sdr[bh * L + j] = sr * g.scale2;
+  sdc[bh * L + j] = sc * g.scale2;
+}
+
+template <typename T, int D>
+static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspace& w, hipStream_t st) {
+  constexpr int EB = Elt<T>::kBytes;
+  const int nbh = g.B * g.H;
+  const size_t BHL = (size_t)nbh * g.L;
+  const int R = f.R;
+  const int nblk = ceil_div_pos(g.L, kBwdBlock);
+  const int grid = (nbh * nblk + 7) & ~7;
+  const int NWC = 16 * (g.TL + g.TR + kBwdWaves);
+  const int NWR = 16 * (g.TLc + g.TRc + kBwdWaves);
+  const size_t row_vec_lds = (size_t)NWC * 4 * 2 + 64;
+  const size_t row_grad_lds = (size_t)NWC * 4 * (1 + 2 * (R > 0 ? R : 1)) + (size_t)D * (NWC + 8) * EB + 64;
+  const size_t col_vec_lds = (size_t)NWR * 4 * 2 + 64;
+  const size_t col_grad_lds = (size_t)NWR * 4 * (1 + 2 * (R > 0 ? R : 1)) + (size_t)D * (NWR + 8) * EB + 64;
+  const size_t col_dv_lds = (size_t)NWR * 4 * 2 + (size_t)D * (NWR + 8) * EB + 64;
+  if (row_grad_lds > 160 * 1024 || col_grad_lds > 160 * 1024 || col_dv_lds > 160 * 1024)
+    return hipErrorInvalidConfiguration;
+  hipError_t err;
+#define SET_LDS(kern, bytes)                                                                              \
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, \
+                            (int)(bytes));                                                                \
+  if (err != hipSuccess) return err;
+  SET_LDS((bw_row_kernel<T, D, 1>), row_grad_lds);
+  SET_LDS((bw_col_kernel<T, D, 1>), col_grad_lds);
+  SET_LDS((bw_col_kernel<T, D, 2>), col_dv_lds);
+#undef SET_LDS
+
+  float* Dv = w.bw;
+  float* vbar = Dv + align64(BHL);
+  float* xv = vbar + align64((size_t)(R + 1) * BHL);
+  BwArgs p{};
+  p.Q = f.Q;
+  p.K = f.K;
+  p.V = f.V;
+  p.dO = f.dO;
+  p.O = f.O;
+  p.a = f.a;
+  p.b = f.b;
+  p.tail_u = w.tail_u;
+  p.tail_v = w.tail_v;
+  p.sdr = w.sdr;
+  p.sdc = w.sdc;
+  p.D = Dv;
+  p.vbar = vbar;
+  p.x = xv;
+  p.R = R;
+  p.padded_grid = grid;
+  const dim3 tg((g.L + 255) / 256, nbh);
+  const T* Qt = reinterpret_cast<const T*>(f.Q);
+  const T* Kt = reinterpret_cast<const T*>(f.K);
+  const T* Vt = reinterpret_cast<const T*>(f.V);
+  const T* dOt = reinterpret_cast<const T*>(f.dO);
+  if (g.dustbin) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
+  hipLaunchKernelGGL(bw_rowdot<T>, tg, dim3(256), 0, st, g, dOt, f.O, Dv);
+  // dV (band) -> add dustbin row, E, vbar^(R)
+  p.out = f.dV;
+  hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
+  hipLaunchKernelGGL(bw_finish_dv<T>, tg, dim3(256), 0, st, g, Vt, dOt, w.tail_u, w.tail_v, w.sdr, R, f.dV,
+                     vbar + (size_t)R * BHL);
+  if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
+  // adjoint vectors through the tail
+  for (int r = R; r >= 1; --r) {
+    p.r = r;
+    hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
+    if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 1);
+    if (r > 1 || f.vbar0) {
+      hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
+      if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 2);
+    }
+  }
+  // dQ, dK
+  p.out = f.dQ;
+  hipLaunchKernelGGL((bw_row_kernel<T, D, 1>), dim3(grid), dim3(256), row_grad_lds, st, g, p);
+  hipLaunchKernelGGL((bw_finish_grad<T, 0>), tg, dim3(256), 0, st, g, p);
+  if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 3);
+  p.out = f.dK;
+  hipLaunchKernelGGL((bw_col_kernel<T, D, 1>), dim3(grid), dim3(256), col_grad_lds, st, g, p);
+  hipLaunchKernelGGL((bw_finish_grad<T, 1>), tg, dim3(256), 0, st, g, p);
+  if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 4);
+  if (f.vbar0) hipLaunchKernelGGL(bw_copy_vbar0, tg, dim3(256), 0, st, g, vbar, f.vbar0);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Geom& g, int dtype, const BwdLaunch& f, const Workspace& w, hipStream_t st) {
+  if (dtype == 0) {
+    switch (g.d) {
+      case 16: return backward_impl<float, 16>(g, f, w, st);
+      case 32: return backward_impl<float, 32>(g, f, w, st);
+      case 64: return backward_impl<float, 64>(g, f, w, st);
+    }
+  } else {
+    switch (g.d) {
+      case 32: return backward_impl<bf16_t, 32>(g, f, w, st);
+      case 64: return backward_impl<bf16_t, 64>(g, f, w, st);
+      case 128: return backward_impl<bf16_t, 128>(g, f, w, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sinkattn

@@ -1,0 +1,130 @@
+// Shared device helpers for the banded Sinkhorn attention kernels (gfx950).
+//
+// Tiles are 16 x 16.  Score tiles come from v_mfma_f32_16x16x32_bf16 (bf16
+// inputs, one instruction per 32-wide k chunk) or v_mfma_f32_16x16x4f32
+// (fp32 inputs, four instructions per 16-wide k chunk).  In both cases a lane
+// feeds 16 contiguous bytes of its operand row per chunk: lane l reads row
+// (l % 16) at byte offset 64 * chunk + 16 * (l / 16).  The k ordering inside
+// a chunk is the same for both operands, so the contraction is exact.
+//
+// Result layout of a 16 x 16 tile C = A B^T (A rows m, B rows n):
+//   lane l holds C[4 * (l / 16) + r][l % 16] in element r (r = 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+
+typedef uint16_t bf16_t;  // storage type of bf16 tensors
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float bits_to_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t float_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 (stored as uint16) -> fp32, exact.
+__device__ __forceinline__ float bf16_to_float(bf16_t h) { return bits_to_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = float_to_bits(f);
+  uint32_t lsb = (u >> 16) & 1u;
+  return (u + 0x7fffu + lsb) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Element-type traits: bytes per element and the score-tile MMA of one chunk.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elt;
+
+template <> struct Elt<float> {
+  static constexpr int kBytes = 4;
+  // 16 contiguous bytes = 4 consecutive k values; four K=4 MFMAs.
+  static __device__ __forceinline__ f4 mma_chunk(f4 acc, u4 a, u4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_float(a.x), bits_to_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_float(a.y), bits_to_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_float(a.z), bits_to_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bits_to_float(a.w), bits_to_float(b.w), acc, 0, 0, 0);
+    return acc;
+  }
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+};
+
+template <> struct Elt<bf16_t> {
+  static constexpr int kBytes = 2;
+  // 16 contiguous bytes = 8 consecutive k values; one K=32 MFMA.
+  static __device__ __forceinline__ f4 mma_chunk(f4 acc, u4 a, u4 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float load(const bf16_t* p, size_t i) { return bf16_to_float(p[i]); }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions.  "row" = the 16 lanes sharing l / 16.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return bits_to_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)float_to_bits(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of each row; every lane receives its row's total.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return x;
+}
+
+// Sum over the four rows (lanes l, l^16, l^32, l^48); every lane gets it.
+__device__ __forceinline__ float cross_row_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ float cross_row_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return cross_row_sum(row16_sum(x)); }
+__device__ __forceinline__ float wave_max(float x) { return cross_row_max(row16_max(x)); }
+
+// ---------------------------------------------------------------------------
+// Global / LDS 16-byte accesses.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u4 ld16(const void* p) { return *reinterpret_cast<const u4*>(p); }
+__device__ __forceinline__ void st16(void* p, u4 v) { *reinterpret_cast<u4*>(p) = v; }
+
+// Map a linear workgroup id to a logical one so that each XCD (ids are dealt
+// to the 8 XCDs round-robin) receives a contiguous range of logical ids:
+// neighbouring band blocks then share that XCD's L2.  `padded` is the launch
+// size (a multiple of 8); logical ids >= the real count are idle.
+__device__ __forceinline__ int xcd_remap(int id, int padded) {
+  const int per = padded >> 3;
+  return (id & 7) * per + (id >> 3);
+}
+
+}  // namespace sinkattn

@@ -1,0 +1,110 @@
+// Band geometry and workspace layout shared by the host launchers and the
+// kernels.  A "strip" is 16 consecutive rows (or columns); a "block" is the
+// 8 strips (128 rows) one workgroup of 8 waves handles.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+constexpr int kStrip = 16;          // rows per strip = MFMA tile edge
+constexpr int kWaves = 8;           // waves per workgroup in the row sweeps
+constexpr int kBlockRows = kStrip * kWaves;  // 128
+constexpr int kMaxTiles = 17;       // register-resident column tiles per strip
+constexpr int kBwdWaves = 4;        // waves per workgroup in the backward sweeps
+constexpr int kBwdBlock = kStrip * kBwdWaves;  // 64
+
+struct Geom {
+  int B, H, L, d;
+  int h1, h2;      // band offsets j - i in [-h1, h2] (clamped to L - 1)
+  int TL, TR;      // column tiles left/right of a row strip's own tile
+  int NT;          // tiles per row strip = TL + TR + 1
+  int TLc, TRc;    // row tiles above/below a column strip's own tile
+  int NTc;         // tiles per column strip = TLc + TRc + 1
+  int nblk;        // 128-row blocks per sequence
+  int NWC;         // window columns of a 128-row block = 16 * (TL + TR + 8)
+  int dustbin;
+  const int* lengths;  // device int32[B] or nullptr
+  float scale2;    // log2(e) / sqrt(d): scores in log2 units
+  float inv_sqrt_d;
+};
+
+__host__ __device__ inline int ceil_div_pos(int a, int b) { return (a + b - 1) / b; }
+
+// Real-token count of sequence bb, clamped so that every index stays in range.
+__device__ inline int real_len(const Geom& g, int bb) {
+  int cap = g.L - (g.dustbin ? 1 : 0);
+  int n = g.lengths ? g.lengths[bb] : cap;
+  n = n < 0 ? 0 : n;
+  return n > cap ? cap : n;
+}
+
+// Workspace carve-up.  Potentials (the Sinkhorn state) are fp64 in log2
+// units; partial sums and backward vectors are fp32.  Sizes in floats.
+struct Workspace {
+  double* tail_u;  // [R+1][BHL] u^(0..R)
+  double* tail_v;  // [R+1][BHL] v^(0..R)
+  double* ubuf;    // [BHL]    latest u
+  double* vbuf;    // [2][BHL] ping-pong v
+  double* dstate;  // [BH][4]  dustbin (u, v, row shift, h)
+  float* part;     // [2][BH][nblk][NWC] column partial sums
+  float* partd;    // [2][BH][nblk]      dustbin-column partial sums
+  float* sdr;      // [BHL] dustbin row scores (log2 units)
+  float* sdc;      // [BHL] dustbin column scores (log2 units)
+  float* bw;       // backward vectors [(3R + 8) * BHL]
+  size_t floats;
+};
+
+inline size_t align64(size_t n) { return (n + 63) & ~size_t(63); }
+
+inline Workspace carve(float* base, const Geom& g, int R) {
+  const size_t BHL = (size_t)g.B * g.H * g.L;
+  const size_t BH = (size_t)g.B * g.H;
+  Workspace w{};
+  size_t off = 0;
+  auto take = [&](size_t n) { float* p = base ? base + off : nullptr; off += align64(n); return p; };
+  auto take_d = [&](size_t n) { return reinterpret_cast<double*>(take(2 * n)); };
+  w.tail_u = take_d((size_t)(R + 1) * BHL);
+  w.tail_v = take_d((size_t)(R + 1) * BHL);
+  w.ubuf = take_d(BHL);
+  w.vbuf = take_d(2 * BHL);
+  w.dstate = take_d(4 * BH);
+  w.part = take(2 * BH * (size_t)g.nblk * g.NWC);
+  w.partd = take(2 * BH * (size_t)g.nblk);
+  w.sdr = take(BHL);
+  w.sdc = take(BHL);
+  w.bw = take((size_t)(3 * R + 8) * BHL);
+  w.floats = off;
+  return w;
+}
+
+// Arguments of the host launchers (device pointers).
+struct FwdLaunch {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* a;
+  const float* b;
+  float* O;
+  float* u;
+  float* v;
+  int T, R;
+};
+
+struct BwdLaunch {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const float* O;
+  const float* a;
+  const float* b;
+  float* dQ;
+  float* dK;
+  float* dV;
+  float* vbar0;
+  int T, R;
+};
+
+}  // namespace sinkattn

@@ -1,0 +1,149 @@
+/*
+ * sinkattn.h -- banded, balanced, log-domain Sinkhorn attention on AMD
+ * Instinct MI355X (gfx950): forward (stopped base + differentiable tail +
+ * output) and the exact tail adjoint.
+ *
+ * The operation follows the summaries of "Blockwise Differentiable Sinkhorn
+ * Attention" (arXiv 2605.08123):
+ *   - section 2.1 (forward pass): attention weights are the entropic
+ *     transport plan on a fixed banded support Omega of width W, with the
+ *     temperature absorbed into S = Q K^T / sqrt(d); T balanced Sinkhorn
+ *     steps run under a stop-gradient (the "stopped base"), then R more steps
+ *     form the differentiable tail; the output is O = P V with
+ *     P = exp(S + u^(R) (+) v^(R)) on Omega.
+ *   - section 2.2 (R = 2 staircase, single reference tile): the backward pass
+ *     is the exact adjoint of the R tail steps; every staircase plan
+ *     P^(a,b) is rebuilt from the reference plan P^(R,R) through the vector
+ *     modifiers exp(u^(a) - u^(R)) and exp(v^(b) - v^(R)), so only O(L)
+ *     extra device memory is used and no L x L or L x W matrix is ever stored.
+ *   - section 2.3 (gap-aware dustbin bridge): a learned dustbin token and
+ *     inactive filler tokens are appended to Q/K/V; the dustbin row and column
+ *     are fully active and the same solver runs on the enlarged state space.
+ *
+ * Conventions (readings where the summaries leave a step open):
+ *   - Band: offsets j - i in [-floor(W/2), ceil(W/2) - 1], clipped at the
+ *     ends of the real tokens (W = 17 is |i - j| <= 8).
+ *   - One step = one row update u_i = log a_i - LSE_{j in Omega_i}(S_ij + v_j)
+ *     followed by one column update v_j = log b_j - LSE_{i}(S_ij + u_i);
+ *     the iteration starts from u = v = 0 and runs exactly T + R steps.
+ *   - Potentials are natural-log, returned raw (no gauge centring).
+ *   - O = P^(R,R) V (raw plan entries, no row renormalisation).
+ *   - Token layout per sequence b: real tokens [0, n_b), then the dustbin at
+ *     index n_b when enabled, then inactive filler up to L.  Filler has zero
+ *     mass and is outside Omega: its u and v are -inf and its rows of O, dQ,
+ *     dK and dV are zero.
+ *
+ * Memory: every pointer is a DEVICE pointer owned by the caller.  The library
+ * allocates nothing and keeps no state between calls; calls on different
+ * streams with different workspaces may run concurrently.  All calls are
+ * stream-ordered and asynchronous; argument validation happens on the host
+ * before anything is enqueued.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every entry point returns one of these; no exceptions
+ * cross the ABI. */
+typedef enum {
+  SINKATTN_OK = 0,
+  SINKATTN_EINVAL = -1,        /* a bad argument (NULL pointer, size, W<1, ...) */
+  SINKATTN_EUNSUPPORTED = -2,  /* valid but outside the built kernels' envelope */
+  SINKATTN_EHIP = -3,          /* a HIP launch or runtime call failed */
+  SINKATTN_EWORKSPACE = -4     /* workspace smaller than sinkattn_workspace_bytes */
+} sinkattn_status;
+
+/* Element type of Q, K, V and dO.  All outputs and potentials are fp32. */
+typedef enum { SINKATTN_F32 = 0, SINKATTN_BF16 = 1 } sinkattn_dtype;
+
+/* Problem shape.
+ *   B, H, L, d : batch, heads, padded sequence length, head dimension.
+ *                Q, K, V, dO, O, dQ, dK, dV are [B, H, L, d], d fastest,
+ *                contiguous, 16-byte aligned.
+ *   dtype      : sinkattn_dtype of Q, K, V and dO.
+ *   lengths    : DEVICE int32[B] real-token counts n_b, or NULL (n_b = L).
+ *                Values are clamped to [0, L] (to [0, L-1] with a dustbin).
+ *   dustbin    : nonzero => token n_b of sequence b is the dustbin; its row
+ *                and column are active against every active token (corner
+ *                included).  Requires n_b < L.
+ * Supported envelope of this build: d in {16, 32, 64} for fp32 and
+ * {32, 64, 128} for bf16; band tile count ceil(W/2 / 16) + floor((15 +
+ * ceil(W/2) - 1) / 16) + 1 <= 17 (W <= 257), or W >= 2L - 1 with L <= 256.
+ * Anything else returns SINKATTN_EUNSUPPORTED. */
+typedef struct {
+  int32_t B, H, L, d;
+  int32_t dtype;
+  const int32_t *lengths;
+  int32_t dustbin;
+} sinkattn_shape;
+
+/* Bytes of device workspace a forward/backward pair needs for (s, W, R).
+ * Layout: [tail stack: u^(0..R) then v^(0..R), each fp64 [B, H, L]]
+ *         [scratch: O(B*H*L) vectors and band-column partial sums].
+ * The size is O(B * H * L * (R + W/128)): no L x W or L x L buffer.
+ * Returns 0 for an invalid shape. */
+size_t sinkattn_workspace_bytes(const sinkattn_shape *s, int W, int R);
+
+/* Byte offset, inside the workspace, of the fp64 [B, H, L] tail-stack slot
+ * u^(r) (is_v = 0) or v^(r) (is_v = 1), r in [0, R].  u^(0), v^(0) is the
+ * stopped base.  Slots hold the potentials in log2 units (natural value
+ * times log2(e)) on active tokens; filler entries are unspecified.
+ * Returns (size_t)-1 for bad arguments. */
+size_t sinkattn_tail_offset(const sinkattn_shape *s, int R, int r, int is_v);
+
+/* Forward pass (sections 2.1 and 2.3).
+ *   Q, K, V     : [B, H, L, d] of s->dtype.
+ *   W           : band width (>= 1).   T : stopped-base steps (>= 0).
+ *   R           : differentiable tail steps (>= 0).
+ *   a, b        : fp32 [B, L] row/column marginals, shared by all heads;
+ *                 positive on active tokens, zero on filler, each summing to 1
+ *                 (contents are the caller's responsibility).
+ *   O           : out, fp32 [B, H, L, d].
+ *   u, v        : out, fp32 [B, H, L] natural-log potentials u^(R), v^(R);
+ *                 -inf on filler.
+ *   workspace   : device buffer of workspace_bytes >=
+ *                 sinkattn_workspace_bytes(s, W, R).  On return (stream order)
+ *                 it holds the tail stack the backward pass needs; keep it
+ *                 unchanged until sinkattn_backward has run.
+ *   stream      : HIP stream (NULL = default stream).
+ * Returns SINKATTN_OK or an error before enqueueing anything. */
+int sinkattn_forward(const void *Q, const void *K, const void *V, int W, int T, int R,
+                     const float *a, const float *b, const sinkattn_shape *s,
+                     float *O, float *u, float *v, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* Backward pass: exact adjoint of the R tail steps with the stopped base held
+ * constant (section 2.2), evaluated with the single-reference-tile schedule.
+ *   Q, K, V, W, T, R, a, b, s : exactly as passed to sinkattn_forward.
+ *   O           : the forward output.   dO : [B, H, L, d] upstream gradient
+ *                 of s->dtype.
+ *   workspace   : the forward's workspace (its tail stack is read; its
+ *                 scratch region is overwritten).
+ *   dQ, dK, dV  : out, fp32 [B, H, L, d] (zero rows on filler).
+ *   vbar0       : optional out (may be NULL), fp32 [B, H, L]: the adjoint
+ *                 that reaches v^(0) and is dropped by the stop-gradient.
+ * Returns SINKATTN_OK or an error before enqueueing anything. */
+int sinkattn_backward(const void *Q, const void *K, const void *V, int W, int T, int R,
+                      const float *a, const float *b, const sinkattn_shape *s,
+                      const float *O, const void *dO, void *workspace,
+                      size_t workspace_bytes, float *dQ, float *dK, float *dV,
+                      float *vbar0, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char *sinkattn_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int sinkattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */

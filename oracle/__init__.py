@@ -13,7 +13,8 @@ Sinkhorn, pure-Python brute force, finite differences and torch autograd.
 
 from .sinkhorn import (  # noqa: F401
     Grads, Solution, Support, adjoint, backward_batch, band_offsets, bptt_batch,
-    col_update, default_processes, forward_batch, output, row_update, scores, solve,
+    col_update, default_processes, forward_backward_batch, forward_batch, output, row_update,
+    scores, solve,
 )
 from .sinkhorn import _Problem as Problem  # noqa: F401
 from .sinkhorn import backward_one, bptt_one, forward_one  # noqa: F401

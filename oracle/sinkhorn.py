@@ -49,7 +49,7 @@ import scipy.sparse as sp
 __all__ = [
     "band_offsets", "Support", "scores", "row_update", "col_update",
     "solve", "Solution", "output", "adjoint", "Grads",
-    "forward_batch", "backward_batch", "bptt_batch",
+    "forward_batch", "backward_batch", "bptt_batch", "forward_backward_batch",
 ]
 
 
@@ -447,6 +447,35 @@ def backward_batch(Q, K, V, a, b, W, T, R, dO, lengths=None, dustbin=False,
     gs = _map(_job_backward, jobs, processes)
     shp = (B, H, L, d)
     return {"dQ": np.stack([g.dQ for g in gs]).reshape(shp),
+            "dK": np.stack([g.dK for g in gs]).reshape(shp),
+            "dV": np.stack([g.dV for g in gs]).reshape(shp),
+            "vbar0": np.stack([g.vbar0 for g in gs]).reshape(B, H, L)}
+
+
+def _job_both(args):
+    q, k, vv, a, b, L, n, W, dustbin, T, R, dO = args
+    sup = Support.build(L, n, W, dustbin)
+    sol = forward_one(q, k, vv, a, b, sup, T, R)
+    return sol, backward_one(q, k, vv, a, b, sup, T, R, dO, sol=sol)
+
+
+def forward_backward_batch(Q, K, V, a, b, W, T, R, dO, lengths=None, dustbin=False,
+                           processes: Optional[int] = None):
+    """forward_batch and backward_batch in one pass (the backward reuses the
+    forward's tail stack instead of re-running the iteration)."""
+    B, H, L, d = Q.shape
+    ns = _lengths_of(L, lengths, B)
+    jobs = [(Q[bi, h], K[bi, h], V[bi, h], a[bi], b[bi], L, ns[bi], W, dustbin, T, R, dO[bi, h])
+            for bi in range(B) for h in range(H)]
+    res = _map(_job_both, jobs, processes)
+    sols = [r[0] for r in res]
+    gs = [r[1] for r in res]
+    shp = (B, H, L, d)
+    us = np.stack([np.stack(s.us) for s in sols], axis=1).reshape(R + 1, B, H, L)
+    vs = np.stack([np.stack(s.vs) for s in sols], axis=1).reshape(R + 1, B, H, L)
+    return {"O": np.stack([s.O for s in sols]).reshape(shp), "u": us[-1], "v": vs[-1],
+            "us": us, "vs": vs,
+            "dQ": np.stack([g.dQ for g in gs]).reshape(shp),
             "dK": np.stack([g.dK for g in gs]).reshape(shp),
             "dV": np.stack([g.dV for g in gs]).reshape(shp),
             "vbar0": np.stack([g.vbar0 for g in gs]).reshape(B, H, L)}

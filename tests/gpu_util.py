@@ -1,0 +1,143 @@
+"""Helpers for GPU-vs-oracle parity tests (imported only by tests)."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def rel_err(x, ref, mask=None):
+    """Normwise relative error ||x - ref|| / ||ref|| over finite reference
+    entries (and `mask` if given); the -inf patterns must agree."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    fin = np.isfinite(ref)
+    if mask is not None:
+        fin &= mask
+    bad = np.isfinite(x) != np.isfinite(ref)
+    if mask is not None:
+        bad &= mask
+    if bad.any():
+        return np.inf
+    den = np.linalg.norm(ref[fin])
+    return float(np.linalg.norm(x[fin] - ref[fin]) / (den if den > 0 else 1.0))
+
+
+def gauge_removed(u, v, active):
+    """(u - c, v + c) with c the mean of u over active entries, per (b, h)."""
+    u = np.array(u, np.float64)
+    v = np.array(v, np.float64)
+    for idx in np.ndindex(u.shape[:-1]):
+        act = active[idx[0]]
+        c = u[idx][act].mean() if act.any() else 0.0
+        u[idx] = np.where(act, u[idx] - c, u[idx])
+        v[idx] = np.where(act, v[idx] + c, v[idx])
+    return u, v
+
+
+def active_mask(prob: workloads.Problem):
+    m = np.zeros((prob.B, prob.L), dtype=bool)
+    for bi, n in enumerate(prob.n_active()):
+        m[bi, :n] = True
+    return m
+
+
+def to_device(prob: workloads.Problem, device="cuda"):
+    import torch
+
+    dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device).to(dt).contiguous()
+
+    d = {"Q": up(prob.Q), "K": up(prob.K), "V": up(prob.V), "dO": up(prob.dO),
+         "a": torch.from_numpy(prob.a).to(device), "b": torch.from_numpy(prob.b).to(device),
+         "lengths": None}
+    if prob.lengths is not None:
+        d["lengths"] = torch.from_numpy(prob.lengths.astype(np.int32)).to(device)
+    return d
+
+
+def run_gpu(prob: workloads.Problem, T=None, R=None, W=None, want_vbar0=False, backward=True):
+    import torch
+
+    import entropic_ot_banded_amd as eoba
+
+    T = prob.T if T is None else T
+    R = prob.R if R is None else R
+    W = prob.W if W is None else W
+    t = to_device(prob)
+    O, u, v, ws = eoba.forward(t["Q"], t["K"], t["V"], W, T, R, t["a"], t["b"], t["lengths"],
+                               prob.dustbin)
+    out = {"O": O, "u": u, "v": v}
+    us, vs = eoba.tail_stack(ws, t["Q"], R, t["lengths"], prob.dustbin)
+    out["us"] = [x.clone() for x in us]
+    out["vs"] = [x.clone() for x in vs]
+    if backward:
+        dQ, dK, dV, vb0 = eoba.backward(t["Q"], t["K"], t["V"], W, T, R, t["a"], t["b"], O, t["dO"],
+                                        ws, t["lengths"], prob.dustbin, want_vbar0)
+        out.update(dQ=dQ, dK=dK, dV=dV)
+        if want_vbar0:
+            out["vbar0"] = vb0
+    torch.cuda.synchronize()
+    res = {}
+    for k, val in out.items():
+        if isinstance(val, list):
+            res[k] = np.stack([x.cpu().numpy() for x in val])
+        else:
+            res[k] = val.float().cpu().numpy()
+    return res
+
+
+def run_oracle(prob: workloads.Problem, T=None, R=None, W=None, backward=True, processes=None):
+    T = prob.T if T is None else T
+    R = prob.R if R is None else R
+    W = prob.W if W is None else W
+    if processes is None:
+        processes = min(16, os.cpu_count() or 1)
+    if backward:
+        return oracle.forward_backward_batch(prob.Q, prob.K, prob.V, prob.a, prob.b, W, T, R,
+                                             prob.dO, prob.lengths, prob.dustbin,
+                                             processes=processes)
+    return oracle.forward_batch(prob.Q, prob.K, prob.V, prob.a, prob.b, W, T, R, prob.lengths,
+                                prob.dustbin, processes=processes)
+
+
+def compare(gpu, ref, prob, keys=("O", "u", "v", "dQ", "dK", "dV")):
+    """Relative errors per output over active tokens, plus the gauge-removed
+    potential pair (O and the plans are invariant under u + c, v - c)."""
+    act = active_mask(prob)
+    act_bhl = np.broadcast_to(act[:, None, :], gpu["u"].shape)
+    act_rows = np.broadcast_to(act[:, None, :, None], gpu["O"].shape)
+    errs = {}
+    for k in keys:
+        if k not in gpu:
+            continue
+        if k in ("u", "v"):
+            errs[k] = rel_err(gpu[k], ref[k], act_bhl)
+        else:
+            errs[k] = rel_err(gpu[k], ref[k], act_rows)
+            # filler rows must be exactly zero
+            if (~act_rows).any():
+                assert np.all(gpu[k][~act_rows] == 0), f"{k}: nonzero filler rows"
+    if "u" in gpu:
+        # gauge-removed pair (u - c, v + c), relative to the raw pair's norm
+        gu, gv = gauge_removed(gpu["u"], gpu["v"], act)
+        ru, rv = gauge_removed(ref["u"], ref["v"], act)
+        num = np.sqrt(np.sum((gu - ru)[act_bhl] ** 2) + np.sum((gv - rv)[act_bhl] ** 2))
+        den = np.sqrt(np.sum(np.asarray(ref["u"], np.float64)[act_bhl] ** 2) +
+                      np.sum(np.asarray(ref["v"], np.float64)[act_bhl] ** 2))
+        errs["uv_gauge"] = float(num / (den if den > 0 else 1.0))
+        # inactive potentials are -inf
+        assert np.all(np.isneginf(gpu["u"][~act_bhl])) and np.all(np.isneginf(gpu["v"][~act_bhl]))
+    return errs
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sinkattn.h declares, and rejects bad arguments on the host before
+enqueueing any work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import entropic_ot_banded_amd as eoba
+from entropic_ot_banded_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from entropic_ot_banded_amd import build
+        build.build()
+    return eoba.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sinkattn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_api():
+    assert _declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert eoba.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert eoba.status_string(code) not in ("ok", "unknown status")
+    assert eoba.status_string(12345) == "unknown status"
+    assert lib.sinkattn_version() >= 10000
+
+
+def _shape(**kw):
+    base = dict(B=1, H=2, L=256, d=64, dtype=binding.SINKATTN_F32, lengths_ptr=0, dustbin=False)
+    base.update(kw)
+    return binding.Shape(**base)
+
+
+def test_workspace_is_linear_in_length(lib):
+    """Extra device memory is O(L) (no L x W or L x L buffer)."""
+    w1 = eoba.workspace_bytes(_shape(L=4096), 128, 2)
+    w2 = eoba.workspace_bytes(_shape(L=8192), 128, 2)
+    assert 1.9 < w2 / w1 < 2.1
+    BHL = 2 * 4096
+    # tail stack (2R+2 vectors) + O(1) vectors per token, far below W floats per token
+    assert w1 < 40 * BHL * 4
+    assert w1 >= (2 * 2 + 2) * BHL * 4
+
+
+def test_workspace_rejects_invalid(lib):
+    assert eoba.workspace_bytes(_shape(d=48), 128, 2) == 0          # unsupported d
+    assert eoba.workspace_bytes(_shape(), 0, 2) == 0                # W < 1
+    assert eoba.workspace_bytes(_shape(), 128, -1) == 0             # R < 0
+    assert eoba.workspace_bytes(_shape(L=0), 128, 2) == 0
+    assert eoba.workspace_bytes(_shape(dtype=7), 128, 2) == 0
+    assert eoba.workspace_bytes(_shape(), 600, 2) == 0              # band too wide for the tiles
+    assert eoba.workspace_bytes(_shape(dtype=binding.SINKATTN_BF16, d=16), 64, 2) == 0
+    assert eoba.workspace_bytes(_shape(dustbin=True), 64, 2) == 0   # dustbin needs lengths
+
+
+def test_tail_offsets(lib):
+    s = _shape(L=100)
+    BHL = 1 * 2 * 100
+    assert eoba.tail_offset(s, 2, 0, False) == 0
+    assert eoba.tail_offset(s, 2, 2, False) == 2 * BHL * 4
+    assert eoba.tail_offset(s, 2, 0, True) >= 3 * BHL * 4
+    assert eoba.tail_offset(s, 2, 3, False) == ctypes.c_size_t(-1).value
+
+
+def _fwd(lib, shape, W=64, T=3, R=2, ws_bytes=None, null=None, misalign=0):
+    fake = 0x10000  # never dereferenced: validation fails first
+    ptrs = {k: ctypes.c_void_p(fake) for k in ("Q", "K", "V", "a", "b", "O", "u", "v", "ws")}
+    if null:
+        ptrs[null] = ctypes.c_void_p(None)
+    if misalign:
+        ptrs["Q"] = ctypes.c_void_p(fake + misalign)
+    s = shape.c()
+    nb = eoba.workspace_bytes(shape, W, R) if ws_bytes is None else ws_bytes
+    return lib.sinkattn_forward(ptrs["Q"], ptrs["K"], ptrs["V"], W, T, R, ptrs["a"], ptrs["b"],
+                                ctypes.byref(s), ptrs["O"], ptrs["u"], ptrs["v"], ptrs["ws"], nb,
+                                ctypes.c_void_p(None))
+
+
+def test_forward_validation_before_launch(lib):
+    sh = _shape()
+    for name in ("Q", "K", "V", "a", "b", "O", "u", "v", "ws"):
+        assert _fwd(lib, sh, null=name) == binding.SINKATTN_EINVAL, name
+    assert _fwd(lib, sh, W=0) == binding.SINKATTN_EINVAL
+    assert _fwd(lib, sh, T=-1) == binding.SINKATTN_EINVAL
+    assert _fwd(lib, sh, R=-2) == binding.SINKATTN_EINVAL
+    assert _fwd(lib, sh, misalign=4) == binding.SINKATTN_EINVAL
+    assert _fwd(lib, _shape(d=40)) == binding.SINKATTN_EUNSUPPORTED
+    assert _fwd(lib, _shape(B=0)) == binding.SINKATTN_EINVAL
+    assert _fwd(lib, sh, ws_bytes=1024) == binding.SINKATTN_EWORKSPACE
+
+
+def test_backward_validation_before_launch(lib):
+    sh = _shape()
+    s = sh.c()
+    fake = ctypes.c_void_p(0x10000)
+    nb = eoba.workspace_bytes(sh, 64, 2)
+    args = [fake, fake, fake, 64, 3, 2, fake, fake, ctypes.byref(s), fake, fake, fake, nb,
+            fake, fake, fake, ctypes.c_void_p(None), ctypes.c_void_p(None)]
+    bad = list(args)
+    bad[10] = ctypes.c_void_p(None)  # dO
+    assert lib.sinkattn_backward(*bad) == binding.SINKATTN_EINVAL
+    bad = list(args)
+    bad[5] = 9  # R beyond the backward's tail limit
+    assert lib.sinkattn_backward(*bad) == binding.SINKATTN_EUNSUPPORTED
+    bad = list(args)
+    bad[12] = 16  # workspace too small
+    assert lib.sinkattn_backward(*bad) == binding.SINKATTN_EWORKSPACE
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        binding.load_library(str(tmp_path / "nope.so"))
