@@ -25,7 +25,8 @@ SINKATTN_F32 = 0
 SINKATTN_BF16 = 1
 
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
-            "sinkattn_backward", "sinkattn_status_string", "sinkattn_version")
+            "sinkattn_backward", "sinkattn_timing_enable", "sinkattn_timing_collect",
+            "sinkattn_status_string", "sinkattn_version")
 
 
 class SinkattnError(RuntimeError):
@@ -64,6 +65,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_backward.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, sz,
                                       vp, vp, vp, vp, vp]
     lib.sinkattn_backward.restype = i32
+    lib.sinkattn_timing_enable.argtypes = [i32]
+    lib.sinkattn_timing_enable.restype = i32
+    lib.sinkattn_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_longlong)]
+    lib.sinkattn_timing_collect.restype = i32
     lib.sinkattn_status_string.argtypes = [i32]
     lib.sinkattn_status_string.restype = ctypes.c_char_p
     lib.sinkattn_version.argtypes = []
@@ -107,6 +113,19 @@ def workspace_bytes(shape: Shape, W: int, R: int) -> int:
 def tail_offset(shape: Shape, R: int, r: int, is_v: bool) -> int:
     s = shape.c()
     return int(load_library().sinkattn_tail_offset(ctypes.byref(s), R, r, 1 if is_v else 0))
+
+
+def timing_enable(on: bool = True):
+    """Start (or stop) per-launch event timing of the fused step kernel."""
+    _check(load_library().sinkattn_timing_enable(1 if on else 0))
+
+
+def timing_collect():
+    """(total_ms, launches) of the fused step kernel since the last collect."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_longlong(0)
+    _check(load_library().sinkattn_timing_collect(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 # ---------------------------------------------------------------------------

@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/sinkattn.h"
 #include "geom.hpp"
@@ -66,7 +67,36 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Diagnostic launch timing: a reusable pool of events, used in pairs.
+struct TimingState {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;  // events recorded since the last collect
+  bool failed = false;
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
 }  // namespace
+
+bool timing_enabled() { return timing().on; }
+
+void timing_mark(hipStream_t st, bool end) {
+  TimingState& t = timing();
+  (void)end;  // events alternate start, end
+  if (t.used == t.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      t.failed = true;
+      return;
+    }
+    t.pool.push_back(e);
+  }
+  if (hipEventRecord(t.pool[t.used], st) != hipSuccess) t.failed = true;
+  ++t.used;
+}
 }  // namespace sinkattn
 
 using namespace sinkattn;
@@ -84,6 +114,40 @@ const char* sinkattn_status_string(int status) {
     case SINKATTN_EWORKSPACE: return "workspace too small";
     default: return "unknown status";
   }
+}
+
+int sinkattn_timing_enable(int on) {
+  TimingState& t = timing();
+  t.on = on != 0;
+  t.used = 0;
+  t.failed = false;
+  return SINKATTN_OK;
+}
+
+int sinkattn_timing_collect(double* total_ms, long long* launches) {
+  if (!total_ms || !launches) return SINKATTN_EINVAL;
+  TimingState& t = timing();
+  double sum = 0.0;
+  long long count = 0;
+  int status = t.failed ? SINKATTN_EHIP : SINKATTN_OK;
+  for (size_t k = 0; k + 1 < t.used; k += 2) {
+    if (hipEventSynchronize(t.pool[k + 1]) != hipSuccess) {
+      status = SINKATTN_EHIP;
+      break;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.pool[k], t.pool[k + 1]) != hipSuccess) {
+      status = SINKATTN_EHIP;
+      break;
+    }
+    sum += ms;
+    ++count;
+  }
+  *total_ms = sum;
+  *launches = count;
+  t.used = 0;
+  t.failed = false;
+  return status;
 }
 
 size_t sinkattn_workspace_bytes(const sinkattn_shape* s, int W, int R) {

@@ -761,7 +761,9 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     a.sdr = w.sdr;
     a.sdc = w.sdc;
     a.padded_grid = grid;
+    if (timing_enabled()) timing_mark(st, false);
     hipLaunchKernelGGL((iter_kernel<T, D>), dim3(grid), dim3(512), iter_lds, st, g, a);
+    if (timing_enabled()) timing_mark(st, true);
     if (g.dustbin) {
       DustArgs da{};
       da.a = f.a;

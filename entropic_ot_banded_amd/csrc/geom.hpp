@@ -3,6 +3,7 @@
 // 8 strips (128 rows) one workgroup of 8 waves handles.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -78,6 +79,12 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.floats = off;
   return w;
 }
+
+// Launch timing of the fused step kernel (diagnostic; see
+// sinkattn_timing_enable).  timing_mark records the start (end = false) or
+// end (end = true) event of one launch on `st`; no-op when disabled.
+bool timing_enabled();
+void timing_mark(hipStream_t st, bool end);
 
 // Arguments of the host launchers (device pointers).
 struct FwdLaunch {
