@@ -51,12 +51,41 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
   x.TL = (h1 + 15) / 16;
   x.TR = (15 + h2) / 16;
   x.NT = x.TL + x.TR + 1;
+  // round the row-sweep tile count up to a compiled instance (3, 5, 9, 17)
+  {
+    const int inst[4] = {3, 5, 9, kMaxTiles};
+    for (int k = 0; k < 4; ++k)
+      if (x.NT <= inst[k]) {
+        x.TR += inst[k] - x.NT;
+        x.NT = inst[k];
+        break;
+      }
+  }
+  // tile t holds offsets [16 (t - TL) - 15, 16 (t - TL) + 15]: interior when
+  // that range lies inside [-h1, h2]
+  {
+    auto fdiv = [](int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+    x.tin_lo = x.TL - fdiv(h1 - 15, 16);
+    x.tin_hi = x.TL + fdiv(h2 - 15, 16);
+  }
   x.TLc = (h2 + 15) / 16;
   x.TRc = (15 + h1) / 16;
   x.NTc = x.TLc + x.TRc + 1;
-  if (x.NT > kMaxTiles || x.NTc > kMaxTiles) return SINKATTN_EUNSUPPORTED;
+  if (x.TL + (15 + h2) / 16 + 1 > kMaxTiles || x.NTc > kMaxTiles) return SINKATTN_EUNSUPPORTED;
   x.nblk = (s->L + kBlockRows - 1) / kBlockRows;
   x.NWC = 16 * (x.TL + x.TR + kWaves);
+  // Segments: a workgroup sweeps SB consecutive blocks so the K window slides
+  // (128 new rows per block) instead of being re-read; aim at one workgroup
+  // per CU.
+  {
+    const long long total = (long long)s->B * s->H * x.nblk;
+    long long sb = (total + kTargetGroups - 1) / kTargetGroups;
+    if (sb < 1) sb = 1;
+    if (sb > x.nblk) sb = x.nblk;
+    x.SB = (int)sb;
+  }
+  x.nseg = (x.nblk + x.SB - 1) / x.SB;
+  x.SW = x.SB * kBlockRows + 16 * (x.TL + x.TR);
   x.dustbin = s->dustbin ? 1 : 0;
   x.lengths = s->lengths;
   x.inv_sqrt_d = 1.0f / std::sqrt((float)s->d);

@@ -518,29 +518,36 @@ __global__ __launch_bounds__(256) void bw_col_kernel(Geom g, BwArgs p) {
 // ---------------------------------------------------------------------------
 // Per-token kernels (one thread per token, d-long loops).
 // ---------------------------------------------------------------------------
+// Per-token kernels below use 16 lanes per token (one DPP row): lane c
+// handles head-dimension columns c, c + 16, ... so row reads coalesce.
+constexpr int kTokPerBlock = 16;  // 256 threads
+
 // D_i = dO_i . O_i on active rows.
 template <typename T>
-__global__ void bw_rowdot(Geom g, const T* dO, const float* O, float* Dv) {
+__global__ __launch_bounds__(256) void bw_rowdot(Geom g, const T* dO, const float* O, float* Dv) {
   const int bh = blockIdx.y;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= g.L) return;
+  const int i = blockIdx.x * kTokPerBlock + (threadIdx.x >> 4);
+  const int c0 = threadIdx.x & 15;
   const int n = real_len(g, bh / g.H);
   const int nact = n + (g.dustbin ? 1 : 0);
-  const size_t o = (size_t)bh * g.L + i;
+  const size_t o = (size_t)bh * g.L + (i < g.L ? i : 0);
   float s = 0.f;
   if (i < nact)
-    for (int c = 0; c < g.d; ++c) s = __builtin_fmaf(Elt<T>::load(dO, o * g.d + c), O[o * g.d + c], s);
-  Dv[o] = s;
+    for (int c = c0; c < g.d; c += 16) s = __builtin_fmaf(Elt<T>::load(dO, o * g.d + c), O[o * g.d + c], s);
+  s = row16_sum(s);
+  if (i < g.L && c0 == 0) Dv[o] = s;
 }
 
 // After the dV sweep: add the dustbin-row entry (delta, j) for real j, zero
 // filler rows, E_j = V_j . dV_j, vbar^(R)_j = E_j.
 template <typename T>
-__global__ void bw_finish_dv(Geom g, const T* V, const T* dO, const double* tail_u, const double* tail_v,
-                             const float* sdr, int R, float* dV, float* vbarR) {
+__global__ __launch_bounds__(256) void bw_finish_dv(Geom g, const T* V, const T* dO, const double* tail_u,
+                                                    const double* tail_v, const float* sdr, int R, float* dV,
+                                                    float* vbarR) {
   const int bh = blockIdx.y;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= g.L) return;
+  const int j = blockIdx.x * kTokPerBlock + (threadIdx.x >> 4);
+  const int c0 = threadIdx.x & 15;
+  if (j >= g.L) return;  // whole 16-lane rows exit together
   const int n = real_len(g, bh / g.H);
   const size_t L = g.L;
   const size_t BHL = (size_t)g.B * g.H * L;
@@ -548,25 +555,26 @@ __global__ void bw_finish_dv(Geom g, const T* V, const T* dO, const double* tail
   const int d = g.d;
   if (j >= n) {
     if (!(g.dustbin && j == n)) {
-      for (int c = 0; c < d; ++c) dV[o * d + c] = 0.f;
-      vbarR[o] = 0.f;
+      for (int c = c0; c < d; c += 16) dV[o * d + c] = 0.f;
+      if (c0 == 0) vbarR[o] = 0.f;
     }
     return;
   }
   float pdj = 0.f;
   if (g.dustbin) {
     const double uRd = tail_u[slot(R, BHL) + bh * L + n];
-    pdj = exp2f(sdr[o] + uRd + tail_v[slot(R, BHL) + o]);
+    pdj = exp2f((float)((double)sdr[o] + uRd + tail_v[slot(R, BHL) + o]));
   }
   const size_t od = (size_t)bh * L + n;
   float e = 0.f;
-  for (int c = 0; c < d; ++c) {
+  for (int c = c0; c < d; c += 16) {
     float dv = dV[o * d + c];
     if (g.dustbin) dv = __builtin_fmaf(pdj, Elt<T>::load(dO, od * d + c), dv);
     dV[o * d + c] = dv;
     e = __builtin_fmaf(Elt<T>::load(V, o * d + c), dv, e);
   }
-  vbarR[o] = e;
+  e = row16_sum(e);
+  if (c0 == 0) vbarR[o] = e;
 }
 
 // After the dQ (IS_K = 0) or dK (IS_K = 1) sweep: add the dustbin entry of
@@ -810,11 +818,12 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   const T* Vt = reinterpret_cast<const T*>(f.V);
   const T* dOt = reinterpret_cast<const T*>(f.dO);
   if (g.dustbin) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
-  hipLaunchKernelGGL(bw_rowdot<T>, tg, dim3(256), 0, st, g, dOt, f.O, Dv);
+  const dim3 tok((g.L + kTokPerBlock - 1) / kTokPerBlock, nbh);
+  hipLaunchKernelGGL(bw_rowdot<T>, tok, dim3(256), 0, st, g, dOt, f.O, Dv);
   // dV (band) -> add dustbin row, E, vbar^(R)
   p.out = f.dV;
   hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
-  hipLaunchKernelGGL(bw_finish_dv<T>, tg, dim3(256), 0, st, g, Vt, dOt, w.tail_u, w.tail_v, w.sdr, R, f.dV,
+  hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, w.tail_u, w.tail_v, w.sdr, R, f.dV,
                      vbar + (size_t)R * BHL);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
   // adjoint vectors through the tail

@@ -96,11 +96,39 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// gfx950 row swaps (a "row" is 16 lanes): permlane32_swap(a, b) returns
+// ([a0, a1, b0, b1], [a2, a3, b2, b3]) and permlane16_swap(a, b) returns
+// ([a0, b0, a2, b2], [a1, b1, a3, b3]) by row.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(float_to_bits(a), float_to_bits(b), false, false);
+  a = bits_to_float(r[0]);
+  b = bits_to_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(float_to_bits(a), float_to_bits(b), false, false);
+  a = bits_to_float(r[0]);
+  b = bits_to_float(r[1]);
+}
+
 // Sum over the four rows (lanes l, l^16, l^32, l^48); every lane gets it.
 __device__ __forceinline__ float cross_row_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  float y = x;
+  swap32(x, y);  // x = [x0, x1, x0, x1], y = [x2, x3, x2, x3]
+  x += y;
+  y = x;
+  swap16(x, y);  // x = [z0, z0, z2, z2], y = [z1, z1, z3, z3]
+  return x + y;
+}
+
+// Four row sums at once: on return row g of the result holds the sum over
+// the four rows of c[g] (c[0..3] are consumed).
+__device__ __forceinline__ float cross_row_sum4(float c0, float c1, float c2, float c3) {
+  swap32(c0, c2);  // c0 = [c0_0, c0_1, c2_0, c2_1], c2 = [c0_2, c0_3, c2_2, c2_3]
+  c0 += c2;
+  swap32(c1, c3);
+  c1 += c3;
+  swap16(c0, c1);  // c0 = [A0, B0, A2, B2], c1 = [A1, B1, A3, B3]
+  return c0 + c1;
 }
 
 __device__ __forceinline__ float cross_row_max(float x) {

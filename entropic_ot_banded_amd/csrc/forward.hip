@@ -47,8 +47,8 @@ struct IterArgs {
   double* v_tail;         // optional copy of v^(t-1)
   double* u_out;          // u^(t), owners write
   double* u_tail;         // optional copy of u^(t)
-  float* part_out;        // [BH][nblk][NWC] column partials of step t
-  float* partd_out;       // [BH][nblk] dustbin-column partials of step t
+  float* part_out;        // [BH][nseg][SW] column partials of step t
+  float* partd_out;       // [BH][nseg] dustbin-column partials of step t
   const double* dstate;   // dustbin state after step t-1 (nullptr => zeros)
   const float* sdr;       // dustbin row scores [BHL], log2 units
   const float* sdc;       // dustbin column scores [BHL], log2 units
@@ -59,278 +59,438 @@ struct IterArgs {
 // floor(a / b) for b > 0 and any sign of a.
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
-// Finish v^(t-1)_j (log2 units, fp64) for band column j (a real token) from
-// the partial sums of step t-1, summed in increasing block order.
+// Ring slot of a global 16-row tile inside a window of NWT tiles.  Windows of
+// consecutive blocks differ by 8 tiles; the tile that enters takes the slot
+// of the tile that leaves.
+__device__ __forceinline__ int ring_tile(int tg, int NWT) {
+  const int m = tg % NWT;
+  return m < 0 ? m + NWT : m;
+}
+
+// Inputs of the column finish for one band column j, gathered early so the
+// loads overlap compute.  Partial sums of step t-1 come from the (at most
+// kMaxSeg) segments whose windows contain j, summed in increasing order.
+constexpr int kMaxSeg = 3;
+struct VIn {
+  double vprev;
+  float b;
+  float part[kMaxSeg];
+  float dust;  // dustbin-row entry of P^(t-1,t-2) (0 without a dustbin)
+};
+
+__device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
+                                        const float* part_in, const float* b, int bb, const double* dstate,
+                                        const float* sdr) {
+  const size_t L = g.L;
+  VIn r;
+  r.vprev = v_prev2 ? v_prev2[bh * L + j] : 0.0;
+  r.b = b[(size_t)bb * L + j];
+  const int segw = g.SB * kBlockRows;
+  const int x = j + 16 * g.TL;
+  int shi = x / segw;
+  shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
+  int slo = floor_div(x - g.SW, segw) + 1;
+  slo = slo < 0 ? 0 : slo;
+#pragma unroll
+  for (int k = 0; k < kMaxSeg; ++k) {
+    const int sg = slo + k;
+    r.part[k] = 0.f;
+    if (sg <= shi && sg * segw < n)  // segments without real rows wrote nothing
+      r.part[k] = part_in[((size_t)bh * g.nseg + sg) * g.SW + (j - (sg * segw - 16 * g.TL))];
+  }
+  r.dust = 0.f;
+  if (g.dustbin && dstate) {
+    const double* ds = dstate + 4 * bh;
+    r.dust = exp2_fast((float)((double)sdr[bh * L + j] + r.vprev - ds[2])) * (float)ds[3];
+  }
+  return r;
+}
+
+// v^(t-1)_j = v^(t-2)_j + log2(b_j / gamma_j), gamma_j = sum_i P^(t-1,t-2)_ij
+// (log2 units, fp64 state; the log of a ratio near 1 is taken in fp32).
+__device__ __forceinline__ double finish_from(const VIn& r) {
+  float gam = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxSeg; ++k) gam += r.part[k];
+  gam += r.dust;
+  return r.vprev + (double)log2f(r.b / gam);
+}
+
 __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
                                            const float* part_in, const float* b, int bb,
                                            const double* dstate, const float* sdr) {
-  const size_t L = g.L;
-  const double vprev = v_prev2 ? v_prev2[bh * L + j] : 0.0;
-  const int x = j + 16 * g.TL - g.NWC;
-  int rlo = floor_div(x, kBlockRows) + 1;
-  rlo = rlo < 0 ? 0 : rlo;
-  int rhi = (j + 16 * g.TL) / kBlockRows;
-  rhi = rhi > g.nblk - 1 ? g.nblk - 1 : rhi;
-  float gam = 0.f;
-  for (int r = rlo; r <= rhi; ++r) {
-    if (r * kBlockRows >= n) break;  // blocks without real rows wrote nothing
-    gam += part_in[((size_t)bh * g.nblk + r) * g.NWC + (j - (r * kBlockRows - 16 * g.TL))];
-  }
-  if (g.dustbin && dstate) {
-    // dustbin row entry of the row-normalised plan P^(t-1,t-2)_{delta j}
-    const double* ds = dstate + 4 * bh;
-    gam += exp2_fast((float)((double)sdr[bh * L + j] + vprev - ds[2])) * (float)ds[3];
-  }
-  return vprev + log2((double)b[(size_t)bb * L + j]) - log2((double)gam);
+  return finish_from(gather_v(g, bh, n, j, v_prev2, part_in, b, bb, dstate, sdr));
 }
 
-template <typename T, int D>
+// One launch = one Sinkhorn step over every (b, h).  A workgroup sweeps a
+// segment of SB consecutive 128-row blocks of one sequence: the K window of
+// a block (NWT tiles of 16 rows) lives in an LDS ring that slides by 8 tiles
+// per block, column partial sums accumulate in LDS across the segment and
+// are written once per column, and the next block's K rows, Q strips and
+// column-finish inputs are fetched into registers while the current block
+// computes.  Inside a strip the tile loop is software-pipelined: the LDS
+// operands of tile t+1 are read and tile t's MFMAs issue before the exp/sum
+// work of tile t-1 runs.  NT (tiles per strip) and the ring size are
+// compile-time; tiles outside the band are masked.
+template <typename T, int D, int NT>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
   constexpr int NCH = RB / 64;             // 16-byte lane chunks per row
   constexpr int RS = RB + 16;              // padded LDS row stride
+  constexpr int PER_ROW = RB / 16;         // 16-byte chunks per row
+  constexpr int NEWLD = (kBlockRows * PER_ROW + 511) / 512;  // chunks per thread per block
+  constexpr int NWT = NT + kWaves - 1;     // ring tiles = window of one block
+  constexpr int NWC = NWT * 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ double sh_vref;
 
   const int nbh = g.B * g.H;
   const int logical = xcd_remap(blockIdx.x, p.padded_grid);
-  if (logical >= nbh * g.nblk) return;
-  const int bh = logical / g.nblk;
-  const int blk = logical - bh * g.nblk;
+  if (logical >= nbh * g.nseg) return;
+  const int bh = logical / g.nseg;
+  const int seg = logical - bh * g.nseg;
   const int bb = bh / g.H;
   const int n = real_len(g, bb);
-  const int r0 = blk * kBlockRows;
-  if (r0 >= n) return;
+  const int b0 = seg * g.SB;
+  if (b0 * kBlockRows >= n) return;
+  int kend = b0 + g.SB;
+  if (kend > g.nblk) kend = g.nblk;
+  {
+    const int kreal = (n + kBlockRows - 1) / kBlockRows;  // blocks holding real rows
+    if (kend > kreal) kend = kreal;
+  }
 
   const size_t L = g.L;
-  const int NWC = g.NWC;
-  const int tw0 = (r0 >> 4) - g.TL;  // first window tile
-  char* kw = smem;                                     // [NWC][RS]
-  float* w2s = reinterpret_cast<float*>(smem + (size_t)NWC * RS);  // [NWC]
-  float* colbuf = w2s + NWC;                           // [8][NWC]
-  float* misc = colbuf + kWaves * NWC;                 // [8]
+  const int seg_r0 = b0 * kBlockRows;
+  const int seg_r1 = seg_r0 + g.SB * kBlockRows;  // owned columns [seg_r0, seg_r1)
+  const int cs = seg_r0 - 16 * g.TL;              // first column of the segment window
+  char* kw = smem;                                              // [NWT ring][16][RS]
+  float* w2s = reinterpret_cast<float*>(smem + (size_t)NWC * RS);  // [NWC] ring, v - vref
+  float* colsum = w2s + NWC;                                    // [NWC] ring, segment sums
+  float* colbuf = colsum + NWC;                                 // [8][NWC] per-wave partials
+  float* misc = colbuf + kWaves * NWC;                          // [8]
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
+  const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
 
-  // (0) reference potential: v^(t-1) at column r0 (a real token)
-  if (tid == 0)
-    sh_vref = p.part_in ? finish_v(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr) : 0.0;
-  __syncthreads();
-  const double vref = sh_vref;
+  // shift reference: v^(t-2) at the segment's first column (any value near
+  // the window's potentials keeps the entries in range)
+  const double vref = p.v_prev2 ? p.v_prev2[bh * L + seg_r0] : 0.0;
 
-  // (1) finish v^(t-1) on the window; owners publish it.
-  for (int c = tid; c < NWC; c += blockDim.x) {
-    const int j = tw0 * 16 + c;
-    float w = kNegInf;
-    if (j >= 0 && j < n) {
-      double vj = 0.0;
-      if (p.part_in) vj = finish_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
-      if (p.v_out && j >= r0 && j < r0 + kBlockRows) {
-        p.v_out[bh * L + j] = vj;
-        if (p.v_tail) p.v_tail[bh * L + j] = vj;
-      }
-      w = (float)(vj - vref);
+  auto publish_v = [&](int j, double vj) {
+    if (p.v_out && j >= seg_r0 && j < seg_r1) {
+      p.v_out[bh * L + j] = vj;
+      if (p.v_tail) p.v_tail[bh * L + j] = vj;
     }
-    w2s[c] = w;
-  }
-  // (2) K window -> LDS (zero outside the real tokens)
+  };
+  auto wrap = [](int x) { return x >= NWT ? x - NWT : x; };  // x in [0, 2 NWT)
+
+  // ring slot of the first window tile of the current block
+  int rb = ring_tile(b0 * 8 - g.TL, NWT);
+
+  // prologue: window of the first block
   {
-    const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
-    const int per_row = RB / 16;
-    for (int idx = tid; idx < NWC * per_row; idx += blockDim.x) {
-      const int row = idx / per_row, c16 = idx - row * per_row;
-      const int j = tw0 * 16 + row;
+    const int jw = (b0 * 8 - g.TL) * 16;
+    for (int c = tid; c < NWC; c += blockDim.x) {
+      const int j = jw + c;
+      const int slot = wrap(rb + (c >> 4)) * 16 + (c & 15);
+      float w = kNegInf;
+      if (j >= 0 && j < n) {
+        double vj = 0.0;
+        if (p.part_in) vj = finish_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
+        publish_v(j, vj);
+        w = (float)(vj - vref);
+      }
+      w2s[slot] = w;
+      colsum[slot] = 0.f;
+    }
+    for (int idx = tid; idx < NWC * PER_ROW; idx += blockDim.x) {
+      const int row = idx / PER_ROW, c16 = idx - row * PER_ROW;
+      const int j = jw + row;
       u4 val = {0u, 0u, 0u, 0u};
       if (j >= 0 && j < n) val = ld16(Kb + (size_t)j * RB + c16 * 16);
-      st16(kw + (size_t)row * RS + c16 * 16, val);
+      st16(kw + (size_t)(wrap(rb + (row >> 4)) * 16 + (row & 15)) * RS + c16 * 16, val);
     }
+    for (int c = tid; c < kWaves * NWC; c += blockDim.x) colbuf[c] = 0.f;
   }
-  float* cb = colbuf + wave * NWC;
-  for (int c = lane; c < NWC; c += 64) cb[c] = 0.f;
-  if (lane == 0) misc[wave] = 0.f;
+  float dust_acc = 0.f;  // dustbin-column partial of the segment (thread 0)
+
+  u4 qa[NCH];
+  auto load_q = [&](int k, u4 (&q)[NCH]) {
+    const int qi = k * kBlockRows + wave * 16 + lr;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      q[c] = (u4){0u, 0u, 0u, 0u};
+      if (qi < n) q[c] = ld16(Qb + (size_t)qi * RB + c * 64 + lg * 16);
+    }
+  };
+  load_q(b0, qa);
   __syncthreads();
 
-  const int i0 = r0 + wave * 16;
-  if (i0 < n) {
-    // Q strip operands (A side: row i0 + lr)
-    u4 qa[NCH];
-    {
-      const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
-      const int qi = i0 + lr;
+  for (int k = b0; k < kend; ++k) {
+    const bool more = k + 1 < kend;
+    // ---- prefetch for block k + 1: 8 new K tiles, column-finish inputs, Q strip
+    const int jn0 = ((k + 1) * 8 + g.TR) * 16;  // first new window row/column
+    u4 knew[NEWLD];
+    VIn vin;
+    u4 qn[NCH];
+    if (more) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        qa[c] = (u4){0u, 0u, 0u, 0u};
-        if (qi < n) qa[c] = ld16(Qb + (size_t)qi * RB + c * 64 + lg * 16);
-      }
-    }
-    const int NT = g.NT;
-    // tile t covers global columns [(tw0 + wave + t) * 16, +16)
-    const int tg0 = tw0 + wave;
-    int t_lo = -tg0;                 // first tile with a column >= 0
-    t_lo = t_lo < 0 ? 0 : t_lo;
-    int t_hi = (n - 1) / 16 - tg0;   // last tile with a column < n
-    t_hi = t_hi > NT - 1 ? NT - 1 : t_hi;
-
-    float e[kMaxTiles][4];
-    float shift[4];
-    float rs[4];
-    float ed[4] = {0.f, 0.f, 0.f, 0.f};
-    bool rowok[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rowok[r] = i0 + 4 * lg + r < n;
-    // dustbin column exponent for the lane's rows, relative to vref
-    float xd[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-    if (g.dustbin) {
-      const double vd = p.dstate ? p.dstate[4 * bh + 1] : 0.0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (rowok[r]) xd[r] = (float)((double)p.sdc[bh * L + i0 + 4 * lg + r] + vd - vref);
-    }
-
-    const bool partial = i0 + 16 > n;  // wave-uniform: strip holds non-real rows
-    // score tile t -> x = S * log2e/sqrt(d) + w_j (band-masked)
-    auto score_tile = [&](int t, float (&x)[4]) {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-      const char* kb = kw + (size_t)((wave + t) * 16 + lr) * RS + lg * 16;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) acc = Elt<T>::mma_chunk(acc, qa[c], ld16(kb + c * 64));
-      const float wj = w2s[(wave + t) * 16 + lr];
-      const int obase = (t - g.TL) * 16 + lr - 4 * lg;
-      const bool interior = (16 * (t - g.TL) - 15 >= -g.h1) && (16 * (t - g.TL) + 15 <= g.h2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = __builtin_fmaf(acc[r], g.scale2, wj);
-        if (!interior) {
-          const int o = obase - r;
-          v = (o >= -g.h1 && o <= g.h2) ? v : kNegInf;
+      for (int e = 0; e < NEWLD; ++e) {
+        const int idx = tid + e * 512;
+        knew[e] = (u4){0u, 0u, 0u, 0u};
+        if (idx < kBlockRows * PER_ROW) {
+          const int j = jn0 + idx / PER_ROW;
+          if (j >= 0 && j < n) knew[e] = ld16(Kb + (size_t)j * RB + (idx % PER_ROW) * 16);
         }
-        if (partial) v = rowok[r] ? v : kNegInf;  // rows past the real tokens
-        x[r] = v;
       }
-    };
+      if (tid < kBlockRows) {
+        const int j = jn0 + tid;
+        if (j >= 0 && j < n && p.part_in) vin = gather_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
+      }
+      load_q(k + 1, qn);
+    }
 
-    bool need_safe = p.first != 0;
-    if (!need_safe) {
+    // ---- block k: one 16-row strip per wave (all strip values wave-uniform)
+    const int i0 = k * kBlockRows + wave * 16;
+    if (i0 < n) {
+      const int rw = wrap(rb + wave);        // ring slot of strip tile t = 0
+      const bool partial = i0 + 16 > n;      // strip holds non-real rows
+      bool rowok[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { shift[r] = 0.f; rs[r] = 0.f; }
+      for (int r = 0; r < 4; ++r) rowok[r] = i0 + 4 * lg + r < n;
+      // dustbin column exponent for the lane's rows, relative to vref
+      float xd[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+      if (g.dustbin) {
+        const double vd = p.dstate ? p.dstate[4 * bh + 1] : 0.0;
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t) {
-        if (t < NT && t >= t_lo && t <= t_hi) {
+        for (int r = 0; r < 4; ++r)
+          if (rowok[r]) xd[r] = (float)((double)p.sdc[bh * L + i0 + 4 * lg + r] + vd - vref);
+      }
+      // Band geometry pinned inside the block loop: the empty asm keeps the
+      // compiler from precomputing every tile's lane masks up front (which
+      // exhausts the scalar registers); recomputing them is a few ops.
+      int TLs = g.TL, h1s = g.h1, h2s = g.h2, tlo = g.tin_lo, thi = g.tin_hi;
+      asm volatile("" : "+s"(TLs), "+s"(h1s), "+s"(h2s), "+s"(tlo), "+s"(thi));
+      // tile t needs per-entry masking when it straddles the band edge or the
+      // strip holds non-real rows
+      auto edge = [&](int t) { return partial || t < tlo || t > thi; };
+      auto masked = [&](int t, float (&x)[4]) {
+        int dl = lr - 4 * lg;
+        asm volatile("" : "+v"(dl));
+        const int obase = (t - TLs) * 16 + dl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int o = obase - r;
+          const bool ok = o >= -h1s && o <= h2s && rowok[r];
+          x[r] = ok ? x[r] : kNegInf;
+        }
+      };
+      auto read_tile = [&](int t, u4 (&kb)[NCH], float& w) {
+        const int rs16 = wrap(rw + t) * 16;
+        const char* src = kw + (size_t)(rs16 + lr) * RS + lg * 16;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kb[c] = ld16(src + c * 64);
+        w = w2s[rs16 + lr];
+      };
+      auto mma_tile = [&](const u4 (&kb)[NCH]) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) acc = Elt<T>::mma_chunk(acc, qa[c], kb[c]);
+        return acc;
+      };
+
+      float e[NT][4];
+      float shift[4] = {0.f, 0.f, 0.f, 0.f};
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      float ed[4] = {0.f, 0.f, 0.f, 0.f};
+      bool need_safe = p.first != 0;
+      if (!need_safe) {
+        // fast path: shift vref only; pipelined MFMA / exp
+        auto consume = [&](int t, const f4& acc, float w) {
           float x[4];
-          score_tile(t, x);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(acc[r], g.scale2, w);
+          if (edge(t)) masked(t, x);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             e[t][r] = exp2_fast(x[r]);
             rs[r] += e[t][r];
           }
-        } else {
+        };
+        u4 kbA[NCH], kbB[NCH];
+        float wA, wB;
+        read_tile(0, kbA, wA);
+        f4 accP = {0.f, 0.f, 0.f, 0.f};
+        float wP = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) e[t][r] = 0.f;
+        for (int t = 0; t < NT; ++t) {
+          if (t & 1) {
+            if (t + 1 < NT) read_tile(t + 1, kbA, wA);
+            const f4 acc = mma_tile(kbB);
+            if (t > 0) consume(t - 1, accP, wP);
+            accP = acc;
+            wP = wB;
+          } else {
+            if (t + 1 < NT) read_tile(t + 1, kbB, wB);
+            const f4 acc = mma_tile(kbA);
+            if (t > 0) consume(t - 1, accP, wP);
+            accP = acc;
+            wP = wA;
+          }
         }
-      }
-      bool bad = false;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rs[r] = row16_sum(rs[r]);
-        if (g.dustbin) {
-          ed[r] = exp2_fast(xd[r]);
-          rs[r] += ed[r];
-        }
-        if (rowok[r]) bad |= !(rs[r] >= 0x1p-120f && rs[r] <= 0x1p120f);
-      }
-      need_safe = __any(bad);
-    }
-    if (need_safe) {
-      // exact per-row maxima
-      float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t) {
-        if (t < NT && t >= t_lo && t <= t_hi) {
-          score_tile(t, e[t]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], e[t][r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) e[t][r] = kNegInf;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        m[r] = row16_max(m[r]);
-        if (g.dustbin) m[r] = fmaxf(m[r], xd[r]);
-        if (!(m[r] > kNegInf)) m[r] = 0.f;  // inactive row
-        shift[r] = m[r];
-        rs[r] = 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t) {
+        consume(NT - 1, accP, wP);
+        bool bad = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          e[t][r] = exp2_fast(e[t][r] - shift[r]);
-          rs[r] += e[t][r];
+          rs[r] = row16_sum(rs[r]);
+          if (g.dustbin) {
+            ed[r] = exp2_fast(xd[r]);
+            rs[r] += ed[r];
+          }
+          if (rowok[r]) bad |= !(rs[r] >= 0x1p-120f && rs[r] <= 0x1p120f);
+        }
+        need_safe = __any(bad);
+      }
+      if (need_safe) {
+        // exact per-row maxima (first step, or entries out of range)
+        float m[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          u4 kb[NCH];
+          float w;
+          read_tile(t, kb, w);
+          const f4 acc = mma_tile(kb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e[t][r] = __builtin_fmaf(acc[r], g.scale2, w);
+          if (edge(t)) masked(t, e[t]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], e[t][r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          m[r] = row16_max(m[r]);
+          if (g.dustbin) m[r] = fmaxf(m[r], xd[r]);
+          if (!(m[r] > kNegInf)) m[r] = 0.f;  // inactive row
+          shift[r] = m[r];
+          rs[r] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[t][r] = exp2_fast(e[t][r] - shift[r]);
+            rs[r] += e[t][r];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          rs[r] = row16_sum(rs[r]);
+          ed[r] = g.dustbin ? exp2_fast(xd[r] - shift[r]) : 0.f;
+          rs[r] += ed[r];
         }
       }
+
+      // u^(t) (fp64 state) and the row weights h_i = a_i / rho_i
+      float h[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        rs[r] = row16_sum(rs[r]);
-        ed[r] = g.dustbin ? exp2_fast(xd[r] - shift[r]) : 0.f;
-        rs[r] += ed[r];
-      }
-    }
-
-    // (3) u^(t) (fp64) and the row weights h_i = a_i / rho_i
-    float h[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * lg + r;
-      h[r] = 0.f;
-      if (rowok[r]) {
-        const float ai = p.a[(size_t)bb * L + i];
-        h[r] = ai / rs[r];
-        if (lr == 0) {
-          const double u = log2((double)ai) - log2((double)rs[r]) - (double)shift[r] - vref;
-          p.u_out[bh * L + i] = u;
-          if (p.u_tail) p.u_tail[bh * L + i] = u;
+        const int i = i0 + 4 * lg + r;
+        h[r] = 0.f;
+        if (rowok[r]) {
+          h[r] = p.a[(size_t)bb * L + i] / rs[r];
+          if (lr == 0) {
+            const double u = (double)log2f(h[r]) - (double)shift[r] - vref;
+            p.u_out[bh * L + i] = u;
+            if (p.u_tail) p.u_tail[bh * L + i] = u;
+          }
         }
       }
-    }
-    // (4) column partials of this strip: sum_i e_ij h_i
-#pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
-      if (t < NT && t >= t_lo && t <= t_hi) {
+      // column partials of this strip, sum_i e_ij h_i, reduced over the four
+      // lane rows four tiles at a time (row g ends with tile t + g's sums)
+      float* cb = colbuf + wave * NWC;
+      auto colp = [&](int t) {
         float cp = e[t][0] * h[0];
         cp = __builtin_fmaf(e[t][1], h[1], cp);
         cp = __builtin_fmaf(e[t][2], h[2], cp);
-        cp = __builtin_fmaf(e[t][3], h[3], cp);
-        cp = cross_row_sum(cp);
-        if (lg == 0) cb[(wave + t) * 16 + lr] = cp;
-      }
-    }
-    if (g.dustbin) {
-      float dp = 0.f;
-      if (lr == 0) {
+        return __builtin_fmaf(e[t][3], h[3], cp);
+      };
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dp = __builtin_fmaf(ed[r], h[r], dp);
+      for (int t = 0; t + 3 < NT; t += 4) {
+        const float s4 = cross_row_sum4(colp(t), colp(t + 1), colp(t + 2), colp(t + 3));
+        cb[wrap(rw + t + lg) * 16 + lr] = s4;
       }
-      dp = wave_sum(dp);
-      if (lane == 0) misc[wave] = dp;
-    }
-  }
-  __syncthreads();
-  // (5) block sums of the column partials, fixed wave order
-  float* po = p.part_out + ((size_t)bh * g.nblk + blk) * NWC;
-  for (int c = tid; c < NWC; c += blockDim.x) {
-    float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += colbuf[w * NWC + c];
-    po[c] = s;
+      for (int t = NT & ~3; t < NT; ++t) {
+        const float s1 = cross_row_sum(colp(t));
+        if (lg == 0) cb[wrap(rw + t) * 16 + lr] = s1;
+      }
+      if (g.dustbin) {
+        float dp = 0.f;
+        if (lr == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dp = __builtin_fmaf(ed[r], h[r], dp);
+        }
+        dp = wave_sum(dp);
+        if (lane == 0) misc[wave] = dp;
+      }
+    } else if (lane == 0) {
+      misc[wave] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- fold the block's partials into the segment sums (fixed wave
+    // order); the 8 tiles that leave the window are complete: flush them.
+    const int tleave = k * 8 - g.TL;  // first global tile leaving after block k
+    for (int c = tid; c < NWC; c += blockDim.x) {
+      float s = colsum[c];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        s += colbuf[w * NWC + c];
+        colbuf[w * NWC + c] = 0.f;
+      }
+      int off = (c >> 4) - rb;  // tile offset within block k's window
+      off = off < 0 ? off + NWT : off;
+      if (off < 8 || !more) {
+        const int j = (tleave + off) * 16 + (c & 15);
+        p.part_out[((size_t)bh * g.nseg + seg) * g.SW + (j - cs)] = s;
+        s = 0.f;
+      }
+      colsum[c] = s;
+    }
+    if (g.dustbin && tid == 0) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) dust_acc += misc[w];
+    }
+    if (more) {
+      // ---- the new tiles take the freed ring slots rb .. rb + 7
+#pragma unroll
+      for (int e = 0; e < NEWLD; ++e) {
+        const int idx = tid + e * 512;
+        if (idx < kBlockRows * PER_ROW) {
+          const int row = idx / PER_ROW;
+          st16(kw + (size_t)(wrap(rb + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, knew[e]);
+        }
+      }
+      if (tid < kBlockRows) {
+        const int j = jn0 + tid;
+        float w = kNegInf;
+        if (j >= 0 && j < n) {
+          const double vj = p.part_in ? finish_from(vin) : 0.0;
+          publish_v(j, vj);
+          w = (float)(vj - vref);
+        }
+        w2s[wrap(rb + (tid >> 4)) * 16 + (tid & 15)] = w;
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) qa[c] = qn[c];
+      rb = wrap(rb + 8);
+    }
+    __syncthreads();
   }
-  if (g.dustbin && tid == 0) {
-    float s = 0.f;
-    for (int w = 0; w < kWaves; ++w) s += misc[w];
-    p.partd_out[(size_t)bh * g.nblk + blk] = s;
-  }
+  if (g.dustbin && tid == 0) p.partd_out[(size_t)bh * g.nseg + seg] = dust_acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -344,7 +504,7 @@ struct DustArgs {
   const float* a;
   const float* b;
   const double* v_cur;  // v^(t-1) on real tokens (nullptr => zeros)
-  const float* partd;   // [BH][nblk] dustbin-column partials of step t
+  const float* partd;   // [BH][nseg] dustbin-column partials of step t
   double* dstate;       // in: state after t-1 (ignored when first); out: after t
   const float* sdr;
   double* u_tail;       // optional: u^(t) slot
@@ -394,7 +554,7 @@ __global__ __launch_bounds__(256) void dustbin_step(Geom g, DustArgs p) {
     const double ud = log2((double)ad) - log2((double)rho) - M;
     const float hd = ad / rho;
     float gam = 0.f;
-    for (int r = 0; r < g.nblk && r * kBlockRows < n; ++r) gam += p.partd[(size_t)bh * g.nblk + r];
+    for (int sg = 0; sg < g.nseg && sg * g.SB * kBlockRows < n; ++sg) gam += p.partd[(size_t)bh * g.nseg + sg];
     gam += exp2_fast((float)((double)srow[n] + vd_prev - M)) * hd;  // corner of P^(t,t-1)
     const double vd = vd_prev + log2((double)bd) - log2((double)gam);
     double* ds = p.dstate + 4 * bh;
@@ -720,12 +880,18 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   const int nbh = g.B * g.H;
   const size_t BHL = (size_t)nbh * g.L;
   const int grid = padded8(nbh * g.nblk);
-  const size_t iter_lds = (size_t)g.NWC * (RB + 16) + (size_t)g.NWC * 4 * (1 + kWaves) + 64;
+  const int iter_grid = padded8(nbh * g.nseg);
+  const size_t iter_lds = (size_t)g.NWC * (RB + 16) + (size_t)g.NWC * 4 * (2 + kWaves) + 64;
   const size_t out_lds = (size_t)g.NWC * 4 + (size_t)D * (g.NWC + 8) * Elt<T>::kBytes + 64;
   hipError_t err;
   if (iter_lds > 150 * 1024 || out_lds > 150 * 1024) return hipErrorInvalidConfiguration;
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(iter_kernel<T, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)iter_lds);
+  // compile-time tile count: the smallest instance covering the band
+  const void* ik;
+  if (g.NT <= 3) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 3>);
+  else if (g.NT <= 5) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 5>);
+  else if (g.NT <= 9) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 9>);
+  else ik = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles>);
+  err = hipFuncSetAttribute(ik, hipFuncAttributeMaxDynamicSharedMemorySize, (int)iter_lds);
   if (err != hipSuccess) return err;
   err = hipFuncSetAttribute(reinterpret_cast<const void*>(output_kernel<T, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
@@ -741,7 +907,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     dim3 zg((g.L + 255) / 256, nbh);
     hipLaunchKernelGGL(zero_start, zg, dim3(256), 0, st, g, w.tail_u, w.tail_v);
   }
-  const size_t part_slot = (size_t)nbh * g.nblk * g.NWC;
+  const size_t part_slot = (size_t)nbh * g.nseg * g.SW;
   for (int t = 1; t <= N; ++t) {
     IterArgs a{};
     a.Q = f.Q;
@@ -756,13 +922,20 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     a.u_out = w.ubuf;
     a.u_tail = (t >= f.T) ? w.tail_u + (size_t)(t - f.T) * BHL : nullptr;
     a.part_out = w.part + (size_t)(t & 1) * part_slot;
-    a.partd_out = w.partd + (size_t)(t & 1) * nbh * g.nblk;
+    a.partd_out = w.partd + (size_t)(t & 1) * nbh * g.nseg;
     a.dstate = (g.dustbin && t > 1) ? w.dstate : nullptr;
     a.sdr = w.sdr;
     a.sdc = w.sdc;
-    a.padded_grid = grid;
+    a.padded_grid = iter_grid;
     if (timing_enabled()) timing_mark(st, false);
-    hipLaunchKernelGGL((iter_kernel<T, D>), dim3(grid), dim3(512), iter_lds, st, g, a);
+    if (g.NT <= 3)
+      hipLaunchKernelGGL((iter_kernel<T, D, 3>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+    else if (g.NT <= 5)
+      hipLaunchKernelGGL((iter_kernel<T, D, 5>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+    else if (g.NT <= 9)
+      hipLaunchKernelGGL((iter_kernel<T, D, 9>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+    else
+      hipLaunchKernelGGL((iter_kernel<T, D, kMaxTiles>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
     if (timing_enabled()) timing_mark(st, true);
     if (g.dustbin) {
       DustArgs da{};

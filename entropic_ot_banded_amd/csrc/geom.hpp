@@ -15,16 +15,22 @@ constexpr int kBlockRows = kStrip * kWaves;  // 128
 constexpr int kMaxTiles = 17;       // register-resident column tiles per strip
 constexpr int kBwdWaves = 4;        // waves per workgroup in the backward sweeps
 constexpr int kBwdBlock = kStrip * kBwdWaves;  // 64
+constexpr int kTargetGroups = 256;  // one segment workgroup per CU of an MI355X
 
 struct Geom {
   int B, H, L, d;
   int h1, h2;      // band offsets j - i in [-h1, h2] (clamped to L - 1)
   int TL, TR;      // column tiles left/right of a row strip's own tile
-  int NT;          // tiles per row strip = TL + TR + 1
+  int NT;          // tiles per row strip = TL + TR + 1 (a compiled instance size;
+                   // TR is extended so, the surplus tiles lie outside the band)
+  int tin_lo, tin_hi;  // strip tiles [tin_lo, tin_hi] lie entirely inside the band
   int TLc, TRc;    // row tiles above/below a column strip's own tile
   int NTc;         // tiles per column strip = TLc + TRc + 1
   int nblk;        // 128-row blocks per sequence
   int NWC;         // window columns of a 128-row block = 16 * (TL + TR + 8)
+  int SB;          // blocks per segment (one workgroup sweeps a segment)
+  int nseg;        // segments per sequence = ceil(nblk / SB)
+  int SW;          // window columns of a segment = SB * 128 + 16 * (TL + TR)
   int dustbin;
   const int* lengths;  // device int32[B] or nullptr
   float scale2;    // log2(e) / sqrt(d): scores in log2 units
@@ -49,8 +55,8 @@ struct Workspace {
   double* ubuf;    // [BHL]    latest u
   double* vbuf;    // [2][BHL] ping-pong v
   double* dstate;  // [BH][4]  dustbin (u, v, row shift, h)
-  float* part;     // [2][BH][nblk][NWC] column partial sums
-  float* partd;    // [2][BH][nblk]      dustbin-column partial sums
+  float* part;     // [2][BH][nseg][SW] column partial sums
+  float* partd;    // [2][BH][nseg]     dustbin-column partial sums
   float* sdr;      // [BHL] dustbin row scores (log2 units)
   float* sdc;      // [BHL] dustbin column scores (log2 units)
   float* bw;       // backward vectors [(3R + 8) * BHL]
@@ -71,8 +77,8 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.ubuf = take_d(BHL);
   w.vbuf = take_d(2 * BHL);
   w.dstate = take_d(4 * BH);
-  w.part = take(2 * BH * (size_t)g.nblk * g.NWC);
-  w.partd = take(2 * BH * (size_t)g.nblk);
+  w.part = take(2 * BH * (size_t)g.nseg * g.SW);
+  w.partd = take(2 * BH * (size_t)g.nseg);
   w.sdr = take(BHL);
   w.sdc = take(BHL);
   w.bw = take((size_t)(3 * R + 8) * BHL);
