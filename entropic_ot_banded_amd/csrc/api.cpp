@@ -67,6 +67,9 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
     auto fdiv = [](int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
     x.tin_lo = x.TL - fdiv(h1 - 15, 16);
     x.tin_hi = x.TL + fdiv(h2 - 15, 16);
+    x.edge_mask = 0u;
+    for (int t = 0; t < x.NT; ++t)
+      if (t < x.tin_lo || t > x.tin_hi) x.edge_mask |= 1u << t;
   }
   x.TLc = (h2 + 15) / 16;
   x.TRc = (15 + h1) / 16;

@@ -75,22 +75,40 @@ struct VIn {
   double vprev;
   float b;
   float part[kMaxSeg];
-  float dust;  // dustbin-row entry of P^(t-1,t-2) (0 without a dustbin)
+  float sdr;       // dustbin-row score s_(delta j) (0 without a dustbin)
+  unsigned valid;  // bit k < kMaxSeg: part[k] comes from a segment window
+                   // holding j; bit kMaxSeg: vprev holds v^(t-2) (else 0)
 };
 
-__device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
-                                        const float* part_in, const float* b, int bb, const double* dstate,
-                                        const float* sdr) {
+// Dustbin state of the previous step that the column finish needs: launch
+// constants of one (b, h).
+struct DustC {
+  int on;
+  double m;   // shift M of the previous step's dustbin row
+  float h;    // a_delta / rho_delta of that row (relative to M)
+};
+
+__device__ __forceinline__ DustC load_dust(const Geom& g, int bh, const double* dstate) {
+  DustC c{0, 0.0, 0.f};
+  if (g.dustbin && dstate) {
+    c.on = 1;
+    c.m = dstate[4 * bh + 2];
+    c.h = (float)dstate[4 * bh + 3];
+  }
+  return c;
+}
+
+// Loads only (no arithmetic on the loaded values), so that issuing it does
+// not make the wave wait for the data.  Column j lies in the windows of the
+// segments [slo, shi].
+__device__ __forceinline__ VIn gather_v_range(const Geom& g, int bh, int n, int j, int slo, int shi,
+                                              const double* v_prev2, const float* part_in, const float* b,
+                                              int bb, const float* sdr) {
   const size_t L = g.L;
+  const int segw = g.SB * kBlockRows;
   VIn r;
   r.vprev = v_prev2 ? v_prev2[bh * L + j] : 0.0;
   r.b = b[(size_t)bb * L + j];
-  const int segw = g.SB * kBlockRows;
-  const int x = j + 16 * g.TL;
-  int shi = x / segw;
-  shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
-  int slo = floor_div(x - g.SW, segw) + 1;
-  slo = slo < 0 ? 0 : slo;
 #pragma unroll
   for (int k = 0; k < kMaxSeg; ++k) {
     const int sg = slo + k;
@@ -98,49 +116,101 @@ __device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, con
     if (sg <= shi && sg * segw < n)  // segments without real rows wrote nothing
       r.part[k] = part_in[((size_t)bh * g.nseg + sg) * g.SW + (j - (sg * segw - 16 * g.TL))];
   }
-  r.dust = 0.f;
-  if (g.dustbin && dstate) {
-    const double* ds = dstate + 4 * bh;
-    r.dust = exp2_fast((float)((double)sdr[bh * L + j] + r.vprev - ds[2])) * (float)ds[3];
-  }
+  r.sdr = g.dustbin ? sdr[bh * L + j] : 0.f;
+  r.valid = (2u << kMaxSeg) - 1;
   return r;
 }
 
+// Same inputs, every load issued unconditionally from an address clamped into
+// its buffer (j in [0, L)); `valid` marks the partials that count.  No
+// branch and no register written before the loads, so a wave issuing them
+// in the middle of other work never waits for earlier loads.
+__device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, int j, int slo, int shi,
+                                                const double* v_prev2, const float* part_in, const float* b,
+                                                int bb, const float* sdr) {
+  const size_t L = g.L;
+  const int segw = g.SB * kBlockRows;
+  VIn r;
+  // v^(t-2) = 0 when v_prev2 is null: load from `b` instead (any readable
+  // address; the finish ignores it), so no branch sits before the loads
+  const double* vp = v_prev2 ? v_prev2 + bh * L : reinterpret_cast<const double*>(b);
+  r.vprev = vp[v_prev2 ? j : 0];
+  r.b = b[(size_t)bb * L + j];
+  r.valid = v_prev2 ? 1u << kMaxSeg : 0u;
+#pragma unroll
+  for (int k = 0; k < kMaxSeg; ++k) {
+    const int sg = slo + k;
+    const bool ok = sg <= shi && sg * segw < n;
+    const int sgc = sg < g.nseg ? sg : g.nseg - 1;
+    int off = j - (sgc * segw - 16 * g.TL);
+    off = off < 0 ? 0 : (off >= g.SW ? g.SW - 1 : off);
+    r.part[k] = part_in[((size_t)bh * g.nseg + sgc) * g.SW + off];
+    r.valid |= (ok ? 1u : 0u) << k;
+  }
+  r.sdr = sdr[bh * L + j];  // always allocated; used only with a dustbin
+  return r;
+}
+
+// Segment s's window covers columns [s segw - 16 TL, s segw - 16 TL + SW).
+__device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
+                                        const float* part_in, const float* b, int bb, const float* sdr) {
+  const int segw = g.SB * kBlockRows;
+  const int x = j + 16 * g.TL;
+  int shi = x / segw;
+  shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
+  int slo = floor_div(x - g.SW, segw) + 1;
+  slo = slo < 0 ? 0 : slo;
+  return gather_v_range(g, bh, n, j, slo, shi, v_prev2, part_in, b, bb, sdr);
+}
+
 // v^(t-1)_j = v^(t-2)_j + log2(b_j / gamma_j), gamma_j = sum_i P^(t-1,t-2)_ij
-// (log2 units, fp64 state; the log of a ratio near 1 is taken in fp32).
-__device__ __forceinline__ double finish_from(const VIn& r) {
+// (log2 units, fp64 state; the log of a ratio near 1 is taken in fp32).  The
+// dustbin row adds its entry of P^(t-1,t-2), exp2(s_(delta j) + v^(t-2)_j - M)
+// times a_delta / rho_delta.
+__device__ __forceinline__ double finish_from(const VIn& r, const DustC& dc) {
+  const double vprev = ((r.valid >> kMaxSeg) & 1u) ? r.vprev : 0.0;
   float gam = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxSeg; ++k) gam += r.part[k];
-  gam += r.dust;
-  return r.vprev + (double)log2f(r.b / gam);
+  for (int k = 0; k < kMaxSeg; ++k) gam += ((r.valid >> k) & 1u) ? r.part[k] : 0.f;
+  if (dc.on) gam += exp2_fast((float)((double)r.sdr + vprev - dc.m)) * dc.h;
+  return vprev + (double)log2f(r.b / gam);
 }
 
 __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
                                            const float* part_in, const float* b, int bb,
                                            const double* dstate, const float* sdr) {
-  return finish_from(gather_v(g, bh, n, j, v_prev2, part_in, b, bb, dstate, sdr));
+  return finish_from(gather_v(g, bh, n, j, v_prev2, part_in, b, bb, sdr), load_dust(g, bh, dstate));
 }
 
 // One launch = one Sinkhorn step over every (b, h).  A workgroup sweeps a
-// segment of SB consecutive 128-row blocks of one sequence: the K window of
-// a block (NWT tiles of 16 rows) lives in an LDS ring that slides by 8 tiles
-// per block, column partial sums accumulate in LDS across the segment and
-// are written once per column, and the next block's K rows, Q strips and
-// column-finish inputs are fetched into registers while the current block
-// computes.  Inside a strip the tile loop is software-pipelined: the LDS
-// operands of tile t+1 are read and tile t's MFMAs issue before the exp/sum
-// work of tile t-1 runs.  NT (tiles per strip) and the ring size are
-// compile-time; tiles outside the band are masked.
+// segment of SB consecutive 128-row blocks of one sequence:
+//  * the K window of a block (NWT tiles of 16 rows) lives in an LDS ring that
+//    slides by 8 tiles per block; each LDS row holds the K row followed by
+//    four copies of w_j = v^(t-1)_j - vref, so a lane reads its tile operand
+//    and its column's w at one address;
+//  * each wave computes one 16-row strip per block; its column partials go
+//    to a per-wave buffer (two buffers, alternating by block), and the fold of
+//    block k-1's partials into the segment's column sums runs during block k,
+//    off the barrier-to-barrier path; a column's sum is written once, when
+//    the column leaves the window;
+//  * the next block's K rows, Q strips, a_i and column-finish inputs are
+//    loaded into registers while the current block computes; the strip issues
+//    no global loads, so those loads stay in flight.
+// NT (tiles per strip) and the ring size are compile-time; tiles that cross
+// the band edge (a host-computed bit mask) or strips with non-real rows are
+// masked per entry.
 template <typename T, int D, int NT>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
   constexpr int NCH = RB / 64;             // 16-byte lane chunks per row
-  constexpr int RS = RB + 16;              // padded LDS row stride
+  constexpr int RS = RB + 80;              // LDS row: K row, w copies at RB + 16 c, pad
+  constexpr int TILEB = 16 * RS;           // bytes per ring tile
   constexpr int PER_ROW = RB / 16;         // 16-byte chunks per row
   constexpr int NEWLD = (kBlockRows * PER_ROW + 511) / 512;  // chunks per thread per block
   constexpr int NWT = NT + kWaves - 1;     // ring tiles = window of one block
   constexpr int NWC = NWT * 16;
+  constexpr int kThreads = 512;            // launch size (a constant: reading blockDim.x is a memory load)
+  static_assert(kBlockRows * PER_ROW == NEWLD * kThreads, "whole 16-byte chunks per thread");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int nbh = g.B * g.H;
@@ -163,17 +233,18 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   const int seg_r0 = b0 * kBlockRows;
   const int seg_r1 = seg_r0 + g.SB * kBlockRows;  // owned columns [seg_r0, seg_r1)
   const int cs = seg_r0 - 16 * g.TL;              // first column of the segment window
-  char* kw = smem;                                              // [NWT ring][16][RS]
-  float* w2s = reinterpret_cast<float*>(smem + (size_t)NWC * RS);  // [NWC] ring, v - vref
-  float* colsum = w2s + NWC;                                    // [NWC] ring, segment sums
-  float* colbuf = colsum + NWC;                                 // [8][NWC] per-wave partials
-  float* misc = colbuf + kWaves * NWC;                          // [8]
+  char* kw = smem;                                                     // [NWC][RS] ring
+  float* colsum = reinterpret_cast<float*>(smem + (size_t)NWC * RS);  // [NWC] segment sums
+  float* colbuf = colsum + NWC;                                        // [2][8][NWC] partials
+  float* misc = colbuf + 2 * kWaves * NWC;                             // [2][8] dustbin partials
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
   const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
+  const DustC dc = load_dust(g, bh, p.dstate);
+  const double vd = (g.dustbin && p.dstate) ? p.dstate[4 * bh + 1] : 0.0;  // v^(t-1)_delta
 
   // shift reference: v^(t-2) at the segment's first column (any value near
   // the window's potentials keeps the entries in range)
@@ -186,97 +257,192 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     }
   };
   auto wrap = [](int x) { return x >= NWT ? x - NWT : x; };  // x in [0, 2 NWT)
+  // the four copies of w in LDS row c (ring slot c / 16)
+  auto put_w = [&](int c, float w) {
+    float* row = reinterpret_cast<float*>(kw + (size_t)c * RS + RB);
+    row[0] = w;
+    row[4] = w;
+    row[8] = w;
+    row[12] = w;
+  };
 
-  // ring slot of the first window tile of the current block
-  int rb = ring_tile(b0 * 8 - g.TL, NWT);
-
-  // prologue: window of the first block
+  // prologue: window of block b0 in ring slots 0 .. NWT-1.  All loads are
+  // issued before any is used (one memory round trip, not one per row group).
   {
+    static_assert(NWC <= kThreads, "one window column per thread");
+    constexpr int PRO = (NWC * PER_ROW + kThreads - 1) / kThreads;
     const int jw = (b0 * 8 - g.TL) * 16;
-    for (int c = tid; c < NWC; c += blockDim.x) {
-      const int j = jw + c;
-      const int slot = wrap(rb + (c >> 4)) * 16 + (c & 15);
+    u4 kv[PRO];
+#pragma unroll
+    for (int e = 0; e < PRO; ++e) {
+      const int idx = tid + e * kThreads;
+      kv[e] = (u4){0u, 0u, 0u, 0u};
+      if (idx < NWC * PER_ROW) {
+        const int j = jw + idx / PER_ROW;
+        if (j >= 0 && j < n) kv[e] = ld16(Kb + (size_t)j * RB + (idx % PER_ROW) * 16);
+      }
+    }
+    const int jc = jw + tid;
+    const bool colok = tid < NWC && jc >= 0 && jc < n;
+    VIn pin;
+    if (colok && p.part_in) pin = gather_v(g, bh, n, jc, p.v_prev2, p.part_in, p.b, bb, p.sdr);
+    if (tid < NWC) {
       float w = kNegInf;
-      if (j >= 0 && j < n) {
-        double vj = 0.0;
-        if (p.part_in) vj = finish_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
-        publish_v(j, vj);
+      if (colok) {
+        const double vj = p.part_in ? finish_from(pin, dc) : 0.0;
+        publish_v(jc, vj);
         w = (float)(vj - vref);
       }
-      w2s[slot] = w;
-      colsum[slot] = 0.f;
+      put_w(tid, w);
+      colsum[tid] = 0.f;
     }
-    for (int idx = tid; idx < NWC * PER_ROW; idx += blockDim.x) {
-      const int row = idx / PER_ROW, c16 = idx - row * PER_ROW;
-      const int j = jw + row;
-      u4 val = {0u, 0u, 0u, 0u};
-      if (j >= 0 && j < n) val = ld16(Kb + (size_t)j * RB + c16 * 16);
-      st16(kw + (size_t)(wrap(rb + (row >> 4)) * 16 + (row & 15)) * RS + c16 * 16, val);
+#pragma unroll
+    for (int e = 0; e < PRO; ++e) {
+      const int idx = tid + e * kThreads;
+      if (idx < NWC * PER_ROW) st16(kw + (size_t)(idx / PER_ROW) * RS + (idx % PER_ROW) * 16, kv[e]);
     }
-    for (int c = tid; c < kWaves * NWC; c += blockDim.x) colbuf[c] = 0.f;
   }
   float dust_acc = 0.f;  // dustbin-column partial of the segment (thread 0)
 
-  u4 qa[NCH];
-  auto load_q = [&](int k, u4 (&q)[NCH]) {
-    const int qi = k * kBlockRows + wave * 16 + lr;
+  // Per-block inputs of the wave's strip, fetched one block ahead: the Q
+  // strip (MFMA B operand) and, for the lane's four rows, a_i and the
+  // dustbin-column score.
+  struct RowIn {
+    u4 q[NCH];
+    float a[4];
+    float sd[4];
+  };
+  // Loads are unconditional from row indices clamped into [0, L): rows past
+  // the sequence only feed entries that the strip masks (rowok).
+  auto load_q_chunk = [&](int k, int c, RowIn& ri) {
+    int qi = k * kBlockRows + wave * 16 + lr;
+    qi = qi < (int)L ? qi : (int)L - 1;
+    ri.q[c] = ld16(Qb + (size_t)qi * RB + c * 64 + lg * 16);
+  };
+  auto load_row_scalars = [&](int k, RowIn& ri) {
+    const int ib = k * kBlockRows + wave * 16 + 4 * lg;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      q[c] = (u4){0u, 0u, 0u, 0u};
-      if (qi < n) q[c] = ld16(Qb + (size_t)qi * RB + c * 64 + lg * 16);
+    for (int r = 0; r < 4; ++r) {
+      const int i = ib + r < (int)L ? ib + r : (int)L - 1;
+      ri.a[r] = p.a[(size_t)bb * L + i];
+      ri.sd[r] = p.sdc[bh * L + i];  // always allocated; used only with a dustbin
     }
   };
-  load_q(b0, qa);
+  RowIn cur;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) load_q_chunk(b0, c, cur);
+  load_row_scalars(b0, cur);
+  // drain the prologue's loads here, so the loop header carries no pending
+  // load (otherwise the first MFMA of every strip waits on all loads in flight)
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // Fold block kf's per-wave partials (buffer bf; its window starts at ring
+  // slot rbf) into the segment sums in wave order; write out the columns
+  // that leave the window after block kf (all of them when `last`).
+  auto fold = [&](int kf, int bf, int rbf, bool last) {
+    for (int c = tid; c < NWC; c += kThreads) {
+      int off = (c >> 4) - rbf;  // tile offset within block kf's window
+      off = off < 0 ? off + NWT : off;
+      float s = colsum[c];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const bool wrote = off >= w && off < w + NT && kf * kBlockRows + 16 * w < n;
+        const float x = colbuf[(bf * kWaves + w) * NWC + c];
+        s += wrote ? x : 0.f;
+      }
+      if (off < 8 || last) {
+        const int j = (kf * 8 - g.TL + off) * 16 + (c & 15);
+        p.part_out[((size_t)bh * g.nseg + seg) * g.SW + (j - cs)] = s;
+        s = 0.f;
+      }
+      colsum[c] = s;
+    }
+    if (g.dustbin && tid == 0) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (kf * kBlockRows + 16 * w < n) dust_acc += misc[bf * kWaves + w];
+    }
+  };
+
+  const char* lane_k = kw + lr * RS + lg * 16;  // lane's operand bytes in ring row lr
+  int jpend = -1;                               // entering column whose v is not yet stored
+  double vpend = 0.0;
+  auto flush_pending = [&]() {
+    if (jpend >= 0) publish_v(jpend, vpend);
+    jpend = -1;
+  };
+  int rb = 0;                                   // ring slot of block k's first window tile
+  int rbp = 0;                                  // same for block k - 1
   for (int k = b0; k < kend; ++k) {
+    const int buf = (k - b0) & 1;
     const bool more = k + 1 < kend;
-    // ---- prefetch for block k + 1: 8 new K tiles, column-finish inputs, Q strip
+    // ---- prefetch for block k + 1 (8 new K tiles, Q strips, a_i, column-
+    // finish inputs) in NPF slices, one issued per tile of the strip's first
+    // tiles: a wave issuing them all at once stalls on the CU's memory pipe.
+    // The loads are unconditional (clamped addresses) so that no register
+    // write on an untaken path makes the compiler wait for them early.
     const int jn0 = ((k + 1) * 8 + g.TR) * 16;  // first new window row/column
     u4 knew[NEWLD];
     VIn vin;
-    u4 qn[NCH];
-    if (more) {
-#pragma unroll
-      for (int e = 0; e < NEWLD; ++e) {
-        const int idx = tid + e * 512;
-        knew[e] = (u4){0u, 0u, 0u, 0u};
-        if (idx < kBlockRows * PER_ROW) {
-          const int j = jn0 + idx / PER_ROW;
-          if (j >= 0 && j < n) knew[e] = ld16(Kb + (size_t)j * RB + (idx % PER_ROW) * 16);
-        }
+    RowIn nxt;
+    constexpr int NPF = NEWLD + NCH + 2;
+    // (issued in the segment's last block too, where nothing uses the values:
+    // every address is clamped into its buffer)
+    auto prefetch = [&](int part) {
+      if (part < NEWLD) {
+        // rows past the sequence are zeroed when stored to LDS
+        const int idx = tid + part * kThreads;
+        int j = jn0 + idx / PER_ROW;
+        j = j < (int)L ? j : (int)L - 1;
+        knew[part] = ld16(Kb + (size_t)j * RB + (idx % PER_ROW) * 16);
+      } else if (part < NEWLD + NCH) {
+        load_q_chunk(k + 1, part - NEWLD, nxt);
+      } else if (part == NEWLD + NCH) {
+        load_row_scalars(k + 1, nxt);
+      } else if (tid < kBlockRows && p.part_in) {
+        // j + 16 TL = (k + 1) 128 + 16 (TL + TR) + tid with tid < 128, so the
+        // first segment window holding j is (k + 1) / SB and the last is at
+        // most two further (16 (TL + TR) <= 256 <= 2 segw)
+        int j = jn0 + tid;
+        const int segw = g.SB * kBlockRows;
+        const int slo = (k + 1) / g.SB;
+        const int x = j + 16 * g.TL;
+        int shi = slo + (x >= (slo + 1) * segw ? 1 : 0) + (x >= (slo + 2) * segw ? 1 : 0);
+        shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
+        j = j < (int)L ? j : (int)L - 1;  // columns past the sequence are not used
+        vin = gather_v_clamped(g, bh, n, j, slo, shi, p.v_prev2, p.part_in, p.b, bb, p.sdr);
       }
-      if (tid < kBlockRows) {
-        const int j = jn0 + tid;
-        if (j >= 0 && j < n && p.part_in) vin = gather_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
-      }
-      load_q(k + 1, qn);
-    }
+    };
+    // ---- partials of block k - 1 into the segment sums
+    if (k > b0) fold(k - 1, buf ^ 1, rbp, false);
 
     // ---- block k: one 16-row strip per wave (all strip values wave-uniform)
     const int i0 = k * kBlockRows + wave * 16;
     if (i0 < n) {
-      const int rw = wrap(rb + wave);        // ring slot of strip tile t = 0
-      const bool partial = i0 + 16 > n;      // strip holds non-real rows
+      // Store the entering columns' v from the previous block now, a whole
+      // strip before the next loop top.  (Waves 0 and 1 hold them; a strip is
+      // skipped only in the segment's last block, after which none is pending
+      // until the final flush.)
+      flush_pending();
+      const int sw = wrap(rb + wave);  // ring slot of strip tile t = 0
+      const bool partial = i0 + 16 > n;
       bool rowok[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) rowok[r] = i0 + 4 * lg + r < n;
       // dustbin column exponent for the lane's rows, relative to vref
       float xd[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
       if (g.dustbin) {
-        const double vd = p.dstate ? p.dstate[4 * bh + 1] : 0.0;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (rowok[r]) xd[r] = (float)((double)p.sdc[bh * L + i0 + 4 * lg + r] + vd - vref);
+          if (rowok[r]) xd[r] = (float)((double)cur.sd[r] + vd - vref);
       }
       // Band geometry pinned inside the block loop: the empty asm keeps the
       // compiler from precomputing every tile's lane masks up front (which
       // exhausts the scalar registers); recomputing them is a few ops.
-      int TLs = g.TL, h1s = g.h1, h2s = g.h2, tlo = g.tin_lo, thi = g.tin_hi;
-      asm volatile("" : "+s"(TLs), "+s"(h1s), "+s"(h2s), "+s"(tlo), "+s"(thi));
-      // tile t needs per-entry masking when it straddles the band edge or the
-      // strip holds non-real rows
-      auto edge = [&](int t) { return partial || t < tlo || t > thi; };
+      int TLs = g.TL, h1s = g.h1, h2s = g.h2;
+      unsigned emask = partial ? 0xffffffffu : g.edge_mask;  // bit t: tile t needs masking
+      asm volatile("" : "+s"(TLs), "+s"(h1s), "+s"(h2s), "+s"(emask));
       auto masked = [&](int t, float (&x)[4]) {
         int dl = lr - 4 * lg;
         asm volatile("" : "+v"(dl));
@@ -289,16 +455,15 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         }
       };
       auto read_tile = [&](int t, u4 (&kb)[NCH], float& w) {
-        const int rs16 = wrap(rw + t) * 16;
-        const char* src = kw + (size_t)(rs16 + lr) * RS + lg * 16;
+        const char* src = lane_k + wrap(sw + t) * TILEB;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) kb[c] = ld16(src + c * 64);
-        w = w2s[rs16 + lr];
+        w = *reinterpret_cast<const float*>(src + RB);
       };
       auto mma_tile = [&](const u4 (&kb)[NCH]) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) acc = Elt<T>::mma_chunk(acc, qa[c], kb[c]);
+        for (int c = 0; c < NCH; ++c) acc = Elt<T>::mma_chunk(acc, cur.q[c], kb[c]);
         return acc;
       };
 
@@ -306,19 +471,24 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       float shift[4] = {0.f, 0.f, 0.f, 0.f};
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
       float ed[4] = {0.f, 0.f, 0.f, 0.f};
+      // The fast pass always runs (it issues the prefetch slices); on the
+      // first step, or when a row sum leaves the safe range, the strip is
+      // recomputed below with exact row maxima.
       bool need_safe = p.first != 0;
-      if (!need_safe) {
+      {
         // fast path: shift vref only; pipelined MFMA / exp
         auto consume = [&](int t, const f4& acc, float w) {
           float x[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(acc[r], g.scale2, w);
-          if (edge(t)) masked(t, x);
+          if ((emask >> t) & 1u) masked(t, x);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             e[t][r] = exp2_fast(x[r]);
             rs[r] += e[t][r];
           }
+          // pin the sums here: otherwise the exps sink below the tile loop
+          asm volatile("" : "+v"(rs[0]), "+v"(rs[1]), "+v"(rs[2]), "+v"(rs[3]));
         };
         u4 kbA[NCH], kbB[NCH];
         float wA, wB;
@@ -327,6 +497,10 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         float wP = 0.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          if (t < NPF) {
+            asm volatile("" ::: "memory");  // keep slice t at tile t (no hoisting)
+            prefetch(t);
+          }
           if (t & 1) {
             if (t + 1 < NT) read_tile(t + 1, kbA, wA);
             const f4 acc = mma_tile(kbB);
@@ -340,8 +514,15 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
             accP = acc;
             wP = wA;
           }
+          // tile t-1's exp/sum work stays in this iteration, interleaved with
+          // tile t's MFMAs and tile t+1's LDS reads (with every exp after the
+          // loop, the LDS/MFMA and VALU phases of all waves run one after
+          // the other)
+          __builtin_amdgcn_sched_barrier(0);
         }
         consume(NT - 1, accP, wP);
+#pragma unroll
+        for (int q = NT; q < NPF; ++q) prefetch(q);
         bool bad = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -352,7 +533,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
           }
           if (rowok[r]) bad |= !(rs[r] >= 0x1p-120f && rs[r] <= 0x1p120f);
         }
-        need_safe = __any(bad);
+        need_safe = need_safe || __any(bad);
       }
       if (need_safe) {
         // exact per-row maxima (first step, or entries out of range)
@@ -365,7 +546,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
           const f4 acc = mma_tile(kb);
 #pragma unroll
           for (int r = 0; r < 4; ++r) e[t][r] = __builtin_fmaf(acc[r], g.scale2, w);
-          if (edge(t)) masked(t, e[t]);
+          if ((emask >> t) & 1u) masked(t, e[t]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], e[t][r]);
         }
@@ -393,24 +574,33 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         }
       }
 
-      // u^(t) (fp64 state) and the row weights h_i = a_i / rho_i
+      // row weights h_i = a_i / rho_i (rho_i lies in [2^-120, 2^120] here)
       float h[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * lg + r;
-        h[r] = 0.f;
-        if (rowok[r]) {
-          h[r] = p.a[(size_t)bb * L + i] / rs[r];
-          if (lr == 0) {
-            const double u = (double)log2f(h[r]) - (double)shift[r] - vref;
-            p.u_out[bh * L + i] = u;
-            if (p.u_tail) p.u_tail[bh * L + i] = u;
+      for (int r = 0; r < 4; ++r) h[r] = rowok[r] ? cur.a[r] * __builtin_amdgcn_rcpf(rs[r]) : 0.f;
+      // u^(t)_i = log2(a_i / rho_i) - c_i - vref (fp64 state), by lane lr = r
+      {
+        const int rsel = lr & 3;
+        float rsv = rs[0], av = cur.a[0], shv = shift[0];
+        bool okv = rowok[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r)
+          if (rsel == r) {
+            rsv = rs[r];
+            av = cur.a[r];
+            shv = shift[r];
+            okv = rowok[r];
           }
+        if (lr < 4 && okv) {
+          const int i = i0 + 4 * lg + rsel;
+          const double u = (double)log2f(av / rsv) - (double)shv - vref;
+          p.u_out[bh * L + i] = u;
+          if (p.u_tail) p.u_tail[bh * L + i] = u;
         }
       }
       // column partials of this strip, sum_i e_ij h_i, reduced over the four
       // lane rows four tiles at a time (row g ends with tile t + g's sums)
-      float* cb = colbuf + wave * NWC;
+      float* cb = colbuf + (buf * kWaves + wave) * NWC;
       auto colp = [&](int t) {
         float cp = e[t][0] * h[0];
         cp = __builtin_fmaf(e[t][1], h[1], cp);
@@ -420,12 +610,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
 #pragma unroll
       for (int t = 0; t + 3 < NT; t += 4) {
         const float s4 = cross_row_sum4(colp(t), colp(t + 1), colp(t + 2), colp(t + 3));
-        cb[wrap(rw + t + lg) * 16 + lr] = s4;
+        cb[wrap(sw + t + lg) * 16 + lr] = s4;
       }
 #pragma unroll
       for (int t = NT & ~3; t < NT; ++t) {
         const float s1 = cross_row_sum(colp(t));
-        if (lg == 0) cb[wrap(rw + t) * 16 + lr] = s1;
+        if (lg == 0) cb[wrap(sw + t) * 16 + lr] = s1;
       }
       if (g.dustbin) {
         float dp = 0.f;
@@ -434,62 +624,46 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
           for (int r = 0; r < 4; ++r) dp = __builtin_fmaf(ed[r], h[r], dp);
         }
         dp = wave_sum(dp);
-        if (lane == 0) misc[wave] = dp;
+        if (lane == 0) misc[buf * kWaves + wave] = dp;
       }
-    } else if (lane == 0) {
-      misc[wave] = 0.f;
+    }
+    // (a wave without a strip occurs only in a segment's last block, where
+    // no prefetched value is used)
+
+    // ---- v^(t-1) of the columns entering with block k + 1 (written to
+    // memory during the next strip: a store still in flight at the loop top
+    // would make the next block's first loads wait for it)
+    float wnew = kNegInf;
+    if (more && tid < kBlockRows) {
+      const int j = jn0 + tid;
+      if (j >= 0 && j < n) {
+        const double vj = p.part_in ? finish_from(vin, dc) : 0.0;
+        jpend = j;
+        vpend = vj;
+        wnew = (float)(vj - vref);
+      }
     }
     __syncthreads();
-
-    // ---- fold the block's partials into the segment sums (fixed wave
-    // order); the 8 tiles that leave the window are complete: flush them.
-    const int tleave = k * 8 - g.TL;  // first global tile leaving after block k
-    for (int c = tid; c < NWC; c += blockDim.x) {
-      float s = colsum[c];
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        s += colbuf[w * NWC + c];
-        colbuf[w * NWC + c] = 0.f;
-      }
-      int off = (c >> 4) - rb;  // tile offset within block k's window
-      off = off < 0 ? off + NWT : off;
-      if (off < 8 || !more) {
-        const int j = (tleave + off) * 16 + (c & 15);
-        p.part_out[((size_t)bh * g.nseg + seg) * g.SW + (j - cs)] = s;
-        s = 0.f;
-      }
-      colsum[c] = s;
-    }
-    if (g.dustbin && tid == 0) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) dust_acc += misc[w];
-    }
     if (more) {
-      // ---- the new tiles take the freed ring slots rb .. rb + 7
+      // ---- the new tiles take the ring slots rb .. rb + 7 that block k freed
 #pragma unroll
       for (int e = 0; e < NEWLD; ++e) {
         const int idx = tid + e * 512;
-        if (idx < kBlockRows * PER_ROW) {
-          const int row = idx / PER_ROW;
-          st16(kw + (size_t)(wrap(rb + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, knew[e]);
-        }
+        const int row = idx / PER_ROW;
+        const int j = jn0 + row;
+        const u4 val = j < n ? knew[e] : (u4){0u, 0u, 0u, 0u};
+        st16(kw + (size_t)(wrap(rb + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, val);
       }
-      if (tid < kBlockRows) {
-        const int j = jn0 + tid;
-        float w = kNegInf;
-        if (j >= 0 && j < n) {
-          const double vj = p.part_in ? finish_from(vin) : 0.0;
-          publish_v(j, vj);
-          w = (float)(vj - vref);
-        }
-        w2s[wrap(rb + (tid >> 4)) * 16 + (tid & 15)] = w;
-      }
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) qa[c] = qn[c];
+      if (tid < kBlockRows) put_w(wrap(rb + (tid >> 4)) * 16 + (tid & 15), wnew);
+      cur = nxt;
+      rbp = rb;
       rb = wrap(rb + 8);
+      __syncthreads();
     }
-    __syncthreads();
   }
+  flush_pending();
+  // the last block's partials; every column still in the window leaves
+  fold(kend - 1, (kend - 1 - b0) & 1, rb, true);
   if (g.dustbin && tid == 0) p.partd_out[(size_t)bh * g.nseg + seg] = dust_acc;
 }
 
@@ -881,10 +1055,10 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   const size_t BHL = (size_t)nbh * g.L;
   const int grid = padded8(nbh * g.nblk);
   const int iter_grid = padded8(nbh * g.nseg);
-  const size_t iter_lds = (size_t)g.NWC * (RB + 16) + (size_t)g.NWC * 4 * (2 + kWaves) + 64;
+  const size_t iter_lds = (size_t)g.NWC * (RB + 80) + (size_t)g.NWC * 4 * (1 + 2 * kWaves) + 2 * kWaves * 4 + 64;
   const size_t out_lds = (size_t)g.NWC * 4 + (size_t)D * (g.NWC + 8) * Elt<T>::kBytes + 64;
   hipError_t err;
-  if (iter_lds > 150 * 1024 || out_lds > 150 * 1024) return hipErrorInvalidConfiguration;
+  if (iter_lds > 160 * 1024 || out_lds > 160 * 1024) return hipErrorInvalidConfiguration;
   // compile-time tile count: the smallest instance covering the band
   const void* ik;
   if (g.NT <= 3) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 3>);

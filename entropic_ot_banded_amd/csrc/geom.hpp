@@ -24,6 +24,7 @@ struct Geom {
   int NT;          // tiles per row strip = TL + TR + 1 (a compiled instance size;
                    // TR is extended so, the surplus tiles lie outside the band)
   int tin_lo, tin_hi;  // strip tiles [tin_lo, tin_hi] lie entirely inside the band
+  unsigned edge_mask;  // bit t set: strip tile t (t < NT) crosses a band edge
   int TLc, TRc;    // row tiles above/below a column strip's own tile
   int NTc;         // tiles per column strip = TLc + TRc + 1
   int nblk;        // 128-row blocks per sequence
