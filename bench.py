@@ -13,6 +13,14 @@ timed per launch with HIP events on its stream) and the float64 oracle timed
 on the host's cores on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--R 2] [--no-cpu-baseline]
+
+Profile summaries (rocprofv3 CSV output -> the text and JSON files kept under
+profiles/):
+
+    python bench.py --summarize DIR
+      DIR/trace: rocprofv3 --kernel-trace --stats --output-format csv run
+      DIR/fetch, DIR/write: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of
+      "bench.py --copy-calibration" (a 256 MiB device copy calibrates both)
 """
 
 from __future__ import annotations
@@ -35,7 +43,10 @@ PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}
 # Transcendental (v_exp_f32) issue rate: 256 CUs x 2.4 GHz x 32 lanes/clk
 # (half the 64-lane fp32 VALU rate per CU).
 PEAK_EXP = 256 * 2.4e9 * 32
+PEAK_HBM = 8.0e12  # bytes/s, published MI355X HBM3E bandwidth
 PMC_FILE = os.path.join(ROOT, "profiles", "iter_kernel_long_context_pmc.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "iter_kernel_long_context.txt")
+COPY_BYTES = 256 << 20  # calibration copy: bytes read and bytes written
 KERNEL_SOURCES = [os.path.join(ROOT, "entropic_ot_banded_amd", "csrc", f)
                   for f in ("forward.hip", "common.hpp", "geom.hpp")]
 
@@ -83,7 +94,37 @@ def work_counts(B, H, L, d, W, T, R):
     return omega, ex_flops, ex_exps, sv_flops, sv_exps
 
 
-def load_pmc(launch_units):
+def step_bytes_per_launch(B, H, L, d, esize, SB, TL, TR, tail=False):
+    """Algorithmic HBM bytes of one fused-step launch: every Q and K row once,
+    a and b, v^(t-2) read, u and v written (fp64), the column partials
+    written and read back (fp32, one per column plus the window overlap of
+    each segment), and the tail copies of u, v on the R tail steps."""
+    tokens = B * H * L
+    per_tok = 2 * d * esize + 4 + 4 + 8 + 8 + 8
+    per_tok += 2 * 4 * (1.0 + 16.0 * (TL + TR) / (SB * 128))
+    if tail:
+        per_tok += 16
+    return tokens * per_tok
+
+
+def step_geometry(B, H, L, W):
+    """Tile geometry the library picks for the fused step (host side of
+    sinkattn_forward): tiles left/right of the diagonal tile, rows per
+    segment in 128-row blocks."""
+    h1 = min(W // 2, L - 1)
+    h2 = min((W + 1) // 2 - 1, L - 1)
+    TL, TR = (h1 + 15) // 16, (15 + h2) // 16
+    NT = TL + TR + 1
+    for inst in (3, 5, 9, 17):
+        if NT <= inst:
+            TR += inst - NT
+            break
+    nblk = (L + 127) // 128
+    SB = min(max(-(-(B * H * nblk) // 256), 1), nblk)
+    return SB, TL, TR
+
+
+def load_pmc(launch_units=None):
     """HBM traffic per launch of the fused step from committed rocprofv3
     counters, scaled by a copy-kernel calibration; None if absent or taken
     on different kernel sources."""
@@ -97,6 +138,81 @@ def load_pmc(launch_units):
     fetch = pmc["fetch_kib_per_dispatch"] * pmc["fetch_scale"]
     write = pmc["write_kib_per_dispatch"] * pmc["write_scale"]
     return (fetch + write) * 1024.0
+
+
+TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d $REPO/gpurun_out/prof/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
+             "--no-cpu-baseline")
+PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
+           "-d $REPO/gpurun_out/prof/{sub} -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 "
+           "--no-cpu-baseline --copy-calibration")
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(d):
+    """Write the profile summaries kept under profiles/ from rocprofv3 CSV
+    output in d/trace (kernel trace + stats), d/fetch and d/write (PMC)."""
+    import glob
+    stats = _csv_rows(glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))[0])
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["Kernel statistics of the long-context workload (B=1, H=8, L=32768, d=128, W=256,",
+             "T=100, R=2, bf16 inputs): 5 timed + 2 warm-up forward+backward steps.",
+             "", "Command ($REPO = repository root):", "  " + TRACE_CMD,
+             "  python3 $REPO/bench.py --summarize $REPO/gpurun_out/prof", "",
+             f"{'calls':>6} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
+    for r in stats[:24]:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+    it = [r for r in stats if "iter_kernel" in r["Name"]]
+    if it:
+        lines += ["", f"fused step (iter_kernel): {int(it[0]['Calls'])} dispatches, average "
+                  f"{float(it[0]['AverageNs']) / 1e3:.2f} us, min {float(it[0]['MinNs']) / 1e3:.2f} us, "
+                  f"max {float(it[0]['MaxNs']) / 1e3:.2f} us"]
+    logf = os.path.join(d, "trace.log")
+    if os.path.exists(logf):
+        for ln in open(logf):
+            if ln.startswith("{"):
+                lines += ["", "bench.py line of the profiled run:", ln.strip()]
+    pmc = {"kernel_source_hash": kernel_source_hash()}
+    for ctr, sub, key in (("FETCH_SIZE", "fetch", "fetch"), ("WRITE_SIZE", "write", "write")):
+        files = glob.glob(os.path.join(d, sub, "*counter_collection.csv"))
+        if not files:
+            continue
+        rows = [r for r in _csv_rows(files[0]) if r["Counter_Name"] == ctr]
+        itv = [float(r["Counter_Value"]) for r in rows if "iter_kernel" in r["Kernel_Name"]]
+        cp = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not itv or not cp:
+            continue
+        copy_kib = max(cp)  # the 256 MiB calibration copy is the largest copy dispatch
+        pmc[f"{key}_kib_per_dispatch"] = sum(itv) / len(itv)
+        pmc[f"{key}_dispatches"] = len(itv)
+        pmc[f"{key}_copy_kib"] = copy_kib
+        pmc[f"{key}_scale"] = (COPY_BYTES / 1024.0) / copy_kib
+        pmc[f"{key}_command"] = PMC_CMD.format(ctr=ctr, sub=sub)
+    if "fetch_scale" in pmc and "write_scale" in pmc:
+        fetch = pmc["fetch_kib_per_dispatch"] * pmc["fetch_scale"] * 1024
+        write = pmc["write_kib_per_dispatch"] * pmc["write_scale"] * 1024
+        SB, TL, TR = step_geometry(1, 8, 32768, 256)
+        alg = step_bytes_per_launch(1, 8, 32768, 128, 2, SB, TL, TR)
+        lines += ["", "HBM traffic of the fused step (rocprofv3 --pmc, one counter per run):",
+                  "  " + pmc["fetch_command"], "  " + pmc["write_command"],
+                  f"  FETCH_SIZE {pmc['fetch_kib_per_dispatch']:.0f} KiB/dispatch x {pmc['fetch_scale']:.3f} "
+                  f"(256 MiB copy read {pmc['fetch_copy_kib']:.0f} KiB) = {fetch / 1e6:.1f} MB",
+                  f"  WRITE_SIZE {pmc['write_kib_per_dispatch']:.0f} KiB/dispatch x {pmc['write_scale']:.3f} "
+                  f"(256 MiB copy wrote {pmc['write_copy_kib']:.0f} KiB) = {write / 1e6:.1f} MB",
+                  f"  total {(fetch + write) / 1e6:.1f} MB per launch; algorithmic {alg / 1e6:.1f} MB "
+                  f"(ratio {(fetch + write) / alg:.3f})",
+                  f"  kernel sources hash {pmc['kernel_source_hash']}"]
+        with open(PMC_FILE, "w") as f:
+            json.dump(pmc, f, indent=1)
+    with open(TRACE_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(prob, heads):
@@ -129,7 +245,11 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSV output")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -197,7 +317,7 @@ def main():
     fwd_ms, bwd_ms = fb[0].elapsed_time(fb[1]), fb[1].elapsed_time(fb[2])
 
     if args.copy_calibration:
-        x = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         y = torch.empty_like(x)
         torch.cuda.synchronize()
         y.copy_(x)
@@ -208,25 +328,30 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
     omega, ex_flops, ex_exps, sv_flops, sv_exps = work_counts(prob.B, prob.H, prob.L, prob.d, W, T, R)
     peak = PEAK_MFMA[prob.dtype]
-    # dominant kernel: the fused Sinkhorn step, 2d flops per band entry per launch
+    # Dominant kernel: the fused Sinkhorn step (T + R launches per forward).
+    # Its tightest roofline is HBM: each launch streams every Q and K row.
     avg_launch_s = (iter_ms / iter_launches) * 1e-3 if iter_launches else float("nan")
+    esize = 2 if prob.dtype == "bf16" else 4
+    SB, TL, TR = step_geometry(prob.B, prob.H, prob.L, W)
+    launch_bytes = step_bytes_per_launch(prob.B, prob.H, prob.L, prob.d, esize, SB, TL, TR)
     launch_flops = omega * 2 * prob.d
-    achieved = launch_flops / avg_launch_s / 1e12
-    traffic = load_pmc(omega)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
+    achieved = launch_bytes / avg_launch_s
+    traffic = load_pmc()
+    roofline = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
                 "traffic": None if traffic is None else round(traffic / 1e9, 4),
                 "kernel": "iter_kernel (fused Sinkhorn step)",
                 "avg_launch_us": round(avg_launch_s * 1e6, 3), "launches": iter_launches,
-                "flops_per_launch": launch_flops,
-                "traffic_unit": "GB per launch",
+                "bytes_per_launch": int(launch_bytes),
+                "traffic_unit": "GB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "mfma_frac": round(launch_flops / avg_launch_s / peak, 4),
                 "exp_frac": round(omega / avg_launch_s / PEAK_EXP, 4)}
     t_s = ms_per_step * 1e-3
     path = {"executed": {"flops": ex_flops, "exps": ex_exps,
                          "frac": round(max(ex_flops / peak, ex_exps / PEAK_EXP) / t_s, 4)},
             "survey_counting": {"flops": sv_flops, "exps": sv_exps,
                                 "frac": round(max(sv_flops / peak, sv_exps / PEAK_EXP) / t_s, 4)},
-            "peak_exp_per_s": PEAK_EXP}
+            "peak_mfma_flops": peak, "peak_exp_per_s": PEAK_EXP}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

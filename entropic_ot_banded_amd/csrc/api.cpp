@@ -103,7 +103,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct TimingState {
   bool on = false;
   std::vector<hipEvent_t> pool;
-  size_t used = 0;  // events recorded since the last collect
+  std::vector<int> launches;  // per bracket (start/end event pair)
+  size_t used = 0;            // events recorded since the last collect
   bool failed = false;
 };
 TimingState& timing() {
@@ -115,9 +116,9 @@ TimingState& timing() {
 
 bool timing_enabled() { return timing().on; }
 
-void timing_mark(hipStream_t st, bool end) {
+void timing_mark(hipStream_t st, bool end, int launches) {
   TimingState& t = timing();
-  (void)end;  // events alternate start, end
+  if (end) t.launches.push_back(launches);  // events alternate start, end
   if (t.used == t.pool.size()) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) {
@@ -152,6 +153,7 @@ int sinkattn_timing_enable(int on) {
   TimingState& t = timing();
   t.on = on != 0;
   t.used = 0;
+  t.launches.clear();
   t.failed = false;
   return SINKATTN_OK;
 }
@@ -173,11 +175,12 @@ int sinkattn_timing_collect(double* total_ms, long long* launches) {
       break;
     }
     sum += ms;
-    ++count;
+    count += k / 2 < t.launches.size() ? t.launches[k / 2] : 1;
   }
   *total_ms = sum;
   *launches = count;
   t.used = 0;
+  t.launches.clear();
   t.failed = false;
   return status;
 }

@@ -89,9 +89,10 @@ inline Workspace carve(float* base, const Geom& g, int R) {
 
 // Launch timing of the fused step kernel (diagnostic; see
 // sinkattn_timing_enable).  timing_mark records the start (end = false) or
-// end (end = true) event of one launch on `st`; no-op when disabled.
+// end (end = true) event of a bracket on `st` covering `launches` step-kernel
+// launches (counted at the end mark); no-op when disabled.
 bool timing_enabled();
-void timing_mark(hipStream_t st, bool end);
+void timing_mark(hipStream_t st, bool end, int launches = 1);
 
 // Arguments of the host launchers (device pointers).
 struct FwdLaunch {

@@ -136,13 +136,14 @@ int sinkattn_backward(const void *Q, const void *K, const void *V, int W, int T,
                       size_t workspace_bytes, float *dQ, float *dK, float *dV,
                       float *vbar0, hipStream_t stream);
 
-/* Diagnostics for benchmarking: per-launch timing of the fused Sinkhorn step
- * kernel, which dominates the run time.  While enabled (on != 0), every
- * launch of that kernel made by sinkattn_forward is bracketed by a pair of
- * HIP events recorded on the caller's stream.  sinkattn_timing_collect waits
- * for the recorded events, writes the summed kernel time in milliseconds and
- * the number of launches since the previous collect (or enable), and resets
- * the counters.  Process-wide state, not thread-safe; events are created
+/* Diagnostics for benchmarking: timing of the fused Sinkhorn step kernel,
+ * which dominates the run time.  While enabled (on != 0), sinkattn_forward
+ * records HIP events on the caller's stream around its step-kernel launches:
+ * one pair around the whole back-to-back run of T + R launches, or (with a
+ * dustbin, whose own kernel runs between steps) one pair per launch.
+ * sinkattn_timing_collect waits for the recorded events, writes the summed
+ * bracketed time in milliseconds and the number of step-kernel launches it
+ * covers since the previous collect (or enable), and resets the counters.  Process-wide state, not thread-safe; events are created
  * lazily and reused.  Returns SINKATTN_OK, SINKATTN_EINVAL (NULL outputs) or
  * SINKATTN_EHIP. */
 int sinkattn_timing_enable(int on);
