@@ -215,23 +215,33 @@ def summarize(d):
     print("\n".join(lines))
 
 
-def cpu_baseline(prob, heads):
-    """The float64 oracle (as is) on `heads` of the H independent heads,
-    single process; scaled to whole-workload tokens/s."""
+def cpu_baseline(prob, heads, length=None):
+    """The float64 oracle (as is) on a bounded sample of the same workload:
+    `heads` of its H independent heads (same input values), all L tokens
+    unless `length` cuts a prefix (then with uniform marginals over the
+    prefix), one process; scaled to whole-workload tokens/s (the work is
+    linear in L and in H)."""
+    import numpy as np
+
     import oracle
     import workloads
 
     sub = workloads.make(5, heads=list(range(heads)), R=prob.R)
+    Ls = sub.L if length is None else min(length, sub.L)
+    sl = lambda x: np.ascontiguousarray(x[:, :, :Ls])
+    a = np.full((sub.B, Ls), 1.0 / Ls, dtype=np.float32)
     t0 = time.perf_counter()
-    oracle.forward_backward_batch(sub.Q, sub.K, sub.V, sub.a, sub.b, sub.W, sub.T, sub.R, sub.dO,
-                                  processes=1)
+    oracle.forward_backward_batch(sl(sub.Q), sl(sub.K), sl(sub.V), a, a.copy(), sub.W, sub.T, sub.R,
+                                  sl(sub.dO), processes=1)
     dt = time.perf_counter() - t0
-    tokens = prob.B * prob.L
-    value = tokens * heads / prob.H / dt
+    # the metric counts a token once for all H heads: the whole workload
+    # (B L tokens, H heads) takes dt * (H / heads) * (L / Ls)
+    value = prob.B * prob.L / (dt * (prob.H / heads) * (prob.L / Ls))
     return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {prob.H} heads (independent problems) of the same workload, "
-                      f"full T={prob.T}, R={prob.R}, forward+backward, float64 numpy/scipy, "
-                      f"1 process; {dt:.1f} s, scaled by H/{heads}",
+            "sample": f"first {Ls} of {prob.L} tokens of {heads} of {prob.H} heads (independent problems) "
+                      f"of the same inputs, uniform marginals over the sample, full T={sub.T}, R={sub.R}, "
+                      f"forward+backward, float64 numpy/scipy, 1 process: {dt:.1f} s; "
+                      f"scaled to the whole workload (work is linear in L and in H)",
             "seconds": dt}
 
 
