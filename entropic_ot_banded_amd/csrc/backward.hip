@@ -765,6 +765,360 @@ __global__ void dustbin_scores_bw(Geom g, const T* Q, const T* K, float* sdr, fl
   sdc[bh * L + j] = sc * g.scale2;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 sweeps for d = 64, 128.  Row sweeps (COL = false): MODE 0 adjoint
+// vector x^(r), MODE 1 dQ.  Column sweeps (COL = true): MODE 0 vbar^(r-1),
+// MODE 1 dK, MODE 2 dV.  Same results as bw_row_kernel / bw_col_kernel.
+//
+// One workgroup of 8 waves per block of 128 strip indices (rows i for row
+// sweeps, columns j for column sweeps); wave w owns strip w (16 indices) and
+// keeps its operands and accumulators in registers.  The block's window of
+// NT + 7 tiles (16 indices of the other side each) streams through LDS two
+// tiles at a time, double-buffered; a wave works on the tiles of its own
+// band span.
+//   score / dP tiles: MFMA 16x16x32, A = streamed tile (row-major LDS),
+//     B = strip registers; a lane of the result holds one strip index and
+//     4 consecutive indices of the other side;
+//   products (dS K, dS^T Q, P^T dO): MFMA 16x16x32 with the tile pair as A
+//     (4 + 4 k-slots per lane, hi + lo bf16) and the streamed rows as B, read
+//     transposed straight from the row-major LDS rows (ds_read_b64_tr_b16:
+//     within 16 lanes, lane 4r + q points at 4 elements of row r, and lane c
+//     receives element c of the 4 rows).
+// Stored rows swizzle their 16-byte chunks (sw_chunk) so that both the
+// 128-bit reads of 8 consecutive rows and the transposed reads of 4
+// consecutive rows are free of bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int kSwWaves = 8;
+constexpr int kSwThreads = 64 * kSwWaves;
+
+__device__ __forceinline__ int sw_chunk(int chunk, int row) {
+  return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+}
+
+__device__ __forceinline__ u2 ld_tr16(const char* p) {
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p));
+  u2 r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
+// hi + lo bf16 operands of 8 fp32 values (4 of tile 0, then 4 of tile 1)
+__device__ __forceinline__ void split_hilo(const float (&v0)[4], const float (&v1)[4], u4& hi, u4& lo) {
+  uint32_t hb[8], lb[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hb[r] = float_to_bf16_bits(v0[r]);
+    hb[4 + r] = float_to_bf16_bits(v1[r]);
+    lb[r] = float_to_bf16_bits(v0[r] - bits_to_float(hb[r] << 16));
+    lb[4 + r] = float_to_bf16_bits(v1[r] - bits_to_float(hb[4 + r] << 16));
+  }
+  hi = (u4){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+  lo = (u4){lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+}
+
+template <int D, bool COL, int MODE>
+__global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) {
+  constexpr int RB = D * 2;           // bytes per row (bf16)
+  constexpr int CPR = RB / 16;        // 16-byte chunks per row
+  constexpr int NCH = RB / 64;        // 32-element MFMA chunks per row
+  constexpr int ND = D / 16;          // 16-wide output slices
+  constexpr int NTEN = MODE == 0 ? 1 : 2;   // streamed tensors
+  constexpr int PT = MODE == 2 ? 1 : 0;     // streamed tensor of the product
+  constexpr int TBYTES = 32 * RB;     // one tile pair of one tensor
+  static_assert(CPR >= 8, "the chunk swizzle needs 8 chunks per row");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int nbh = g.B * g.H;
+  const int nblk = ceil_div_pos(g.L, 128);
+  const int logical = xcd_remap(blockIdx.x, p.padded_grid);
+  if (logical >= nbh * nblk) return;
+  const int bh = logical / nblk;
+  const int blk = logical - bh * nblk;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const int s0b = blk * 128;
+  if (s0b >= n) return;
+  const size_t L = g.L;
+  const size_t BHL = (size_t)nbh * L;
+  const int R = p.R;
+  const int TLx = COL ? g.TLc : g.TL;
+  const int NT = COL ? g.NTc : g.NT;
+  const int NW = NT + kSwWaves - 1;   // window tiles of the block
+  const int NP = (NW + 1) >> 1;       // tile pairs
+  const int NWC = 2 * NP * 16;        // window indices held in LDS
+  const int tw0 = blk * 8 - TLx;      // first window tile (global)
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+
+  // LDS: tiles [2 buffers][NTEN][32 rows][RB] | wv [NWC] | window vectors [NV][NWC]
+  constexpr int NVMAX = 2 * kMaxR;
+  char* tbuf = smem;
+  float* wv = reinterpret_cast<float*>(smem + 2 * NTEN * TBYTES);
+  float* vec = wv + NWC;
+  const int NV = MODE == 0 ? 1 : (MODE == 1 ? 2 * R : 0);
+
+  const double* uR = p.tail_u + slot(R, BHL) + bh * L;
+  const double* vR = p.tail_v + slot(R, BHL) + bh * L;
+  // exponent split: strip side (x_s + ref) + window side (x_w - ref)
+  const double ref = COL ? uR[s0b] : vR[s0b];
+  for (int c = tid; c < NWC; c += kSwThreads) {
+    const int k = tw0 * 16 + c;  // window index (a column j for row sweeps, a row i for column sweeps)
+    const bool ok = k >= 0 && k < n;
+    wv[c] = ok ? (float)((COL ? uR[k] : vR[k]) - ref) : kNegInf;
+    if (MODE == 0) {
+      float z = 0.f;
+      if (ok) {
+        if (COL)  // zz_i = alpha^(r)_i x^(r)_i
+          z = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + k] - uR[k]) * p.x[slot(p.r, BHL) + bh * L + k];
+        else  // z_j = beta^(r)_j y^(r)_j
+          z = exp2f(p.tail_v[slot(p.r, BHL) + bh * L + k] - vR[k]) * p.vbar[slot(p.r, BHL) + bh * L + k] /
+              p.b[(size_t)bb * L + k];
+      }
+      vec[c] = z;
+    } else if (MODE == 1) {
+      for (int kk = 1; kk <= R; ++kk) {
+        float m0 = 0.f, m1 = 0.f;
+        if (ok) {
+          if (COL) {  // row modifiers alpha^(k)_i, alpha^(k)_i x^(k)_i
+            m0 = exp2f(p.tail_u[slot(kk, BHL) + bh * L + k] - uR[k]);
+            m1 = m0 * p.x[slot(kk, BHL) + bh * L + k];
+          } else {  // column modifiers beta^(k)_j y^(k)_j, beta^(k-1)_j
+            m0 = exp2f(p.tail_v[slot(kk, BHL) + bh * L + k] - vR[k]) * p.vbar[slot(kk, BHL) + bh * L + k] /
+                 p.b[(size_t)bb * L + k];
+            m1 = exp2f(p.tail_v[slot(kk - 1, BHL) + bh * L + k] - vR[k]);
+          }
+        }
+        vec[(size_t)(2 * (kk - 1)) * NWC + c] = m0;
+        vec[(size_t)(2 * (kk - 1) + 1) * NWC + c] = m1;
+      }
+    }
+  }
+  (void)NVMAX;
+  (void)NV;
+
+  // streamed tensors: [0] score side (K rows / Q rows), [1] dP side (V / dO)
+  // or, for dV, the product side (dO)
+  const char* X0 = reinterpret_cast<const char*>(COL ? p.Q : p.K) + (size_t)bh * L * RB;
+  const char* X1 = reinterpret_cast<const char*>(COL ? p.dO : p.V) + (size_t)bh * L * RB;
+  // one 16-byte chunk per thread per tensor and pair (rows clamped into
+  // [0, L); rows outside [0, n) are stored as zeros)
+  u4 pre[NTEN];
+  int pre_row = 0;
+  auto load_pair = [&](int pp) {
+    const int idx = tid;  // < 32 * CPR when CPR == 16; guarded otherwise
+    const int r32 = idx / CPR;
+    int grow = (tw0 + 2 * pp) * 16 + r32;
+    pre_row = grow;
+    grow = grow < 0 ? 0 : (grow >= (int)L ? (int)L - 1 : grow);
+    if (idx < 32 * CPR) {
+      pre[0] = ld16(X0 + (size_t)grow * RB + (idx % CPR) * 16);
+      if (NTEN > 1) pre[NTEN - 1] = ld16(X1 + (size_t)grow * RB + (idx % CPR) * 16);
+    }
+  };
+  auto store_pair = [&](int buf) {
+    const int idx = tid;
+    if (idx < 32 * CPR) {
+      const int r32 = idx / CPR, c16 = idx % CPR;
+      const bool ok = pre_row >= 0 && pre_row < n;
+      const int off = r32 * RB + sw_chunk(c16, r32) * 16;
+#pragma unroll
+      for (int te = 0; te < NTEN; ++te) {
+        const u4 v = ok ? pre[te] : (u4){0u, 0u, 0u, 0u};
+        st16(tbuf + (size_t)(buf * NTEN + te) * TBYTES + off, v);
+      }
+    }
+  };
+
+  // strip operands (registers): score side (Q rows / K rows), dP side (dO / V)
+  const int si = s0b + wave * 16 + lr;  // strip index of this lane (B operand row)
+  const bool sok = si < n;
+  const int sic = si < (int)L ? si : (int)L - 1;
+  const char* S0 = reinterpret_cast<const char*>(COL ? p.K : p.Q) + (size_t)bh * L * RB;
+  const char* S1 = reinterpret_cast<const char*>(COL ? p.V : p.dO) + (size_t)bh * L * RB;
+  u4 sb0[NCH], sb1[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u4 a0 = ld16(S0 + (size_t)sic * RB + c * 64 + lg * 16);
+    sb0[c] = sok ? a0 : (u4){0u, 0u, 0u, 0u};
+    if (MODE == 1) {
+      const u4 a1 = ld16(S1 + (size_t)sic * RB + c * 64 + lg * 16);
+      sb1[c] = sok ? a1 : (u4){0u, 0u, 0u, 0u};
+    }
+  }
+  // strip-side exponent part and strip modifiers (MODE 1)
+  const float sbias = sok ? (float)((COL ? vR[si] : uR[si]) + ref) : 0.f;
+  float sm0[kMaxR], sm1[kMaxR];
+#pragma unroll
+  for (int k = 0; k < kMaxR; ++k) {
+    sm0[k] = 0.f;
+    sm1[k] = 0.f;
+    if (MODE == 1 && k < R && sok) {
+      if (COL) {  // beta^(k)_j y^(k)_j, beta^(k-1)_j
+        sm0[k] = exp2f(p.tail_v[slot(k + 1, BHL) + bh * L + si] - vR[si]) * p.vbar[slot(k + 1, BHL) + bh * L + si] /
+                 p.b[(size_t)bb * L + si];
+        sm1[k] = exp2f(p.tail_v[slot(k, BHL) + bh * L + si] - vR[si]);
+      } else {  // alpha^(k)_i, alpha^(k)_i x^(k)_i
+        sm0[k] = exp2f(p.tail_u[slot(k + 1, BHL) + bh * L + si] - uR[si]);
+        sm1[k] = sm0[k] * p.x[slot(k + 1, BHL) + bh * L + si];
+      }
+    }
+  }
+
+  // per-lane LDS offsets: A-operand chunks of row lr; transposed B reads
+  int offA[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) offA[c] = lr * RB + sw_chunk(4 * c + lg, lr) * 16;
+  int offB[ND];
+  {
+    const int m = lr;  // lane within its 16-lane group; group = lg
+    const int row = 4 * lg + (m >> 2);
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) offB[ds] = row * RB + sw_chunk(2 * ds + ((m & 3) >> 1), row) * 16 + 8 * (m & 1);
+  }
+
+  float vacc = 0.f;  // MODE 0
+  f4 acc[ND];
+#pragma unroll
+  for (int ds = 0; ds < ND; ++ds) acc[ds] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  load_pair(0);
+  store_pair(0);
+  if (NP > 1) load_pair(1);
+  __syncthreads();
+
+  const int wstart = wave;           // first window tile of this strip
+  const int sidx0 = s0b + wave * 16;  // first strip index of the wave
+  const bool wactive = sidx0 < n;
+  for (int pp = 0; pp < NP; ++pp) {
+    const int buf = pp & 1;
+    if (pp + 1 < NP) {
+      store_pair(buf ^ 1);             // pair pp + 1 (loaded one step ago)
+      if (pp + 2 < NP) load_pair(pp + 2);
+    }
+    // tiles 2pp, 2pp + 1 of the window; strip-relative t = window tile - wave
+    float val[2][4];
+    bool any = false;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int wt = 2 * pp + tt;
+      const int t = wt - wstart;
+      const int tg = tw0 + wt;  // global tile
+      const bool act = wactive && t >= 0 && t < NT && tg >= 0 && tg * 16 < n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) val[tt][r] = 0.f;
+      if (act) {
+        any = true;
+        const char* tb0 = tbuf + (size_t)(buf * NTEN + 0) * TBYTES + tt * 16 * RB;
+        f4 sacc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const u4 a = ld16(tb0 + offA[c]);
+          sacc = Elt<bf16_t>::mma_chunk(sacc, a, sb0[c]);
+        }
+        if (MODE == 1) {
+          const char* tb1 = tbuf + (size_t)(buf * NTEN + 1) * TBYTES + tt * 16 * RB;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const u4 a = ld16(tb1 + offA[c]);
+            dacc = Elt<bf16_t>::mma_chunk(dacc, a, sb1[c]);
+          }
+        }
+        // lane: strip index si, window indices wi = tg * 16 + 4 lg + r
+        const int cw = wt * 16 + 4 * lg;  // window position of r = 0
+        const f4 w4 = *reinterpret_cast<const f4*>(wv + cw);
+        f4 z4 = {0.f, 0.f, 0.f, 0.f};
+        if (MODE == 0) z4 = *reinterpret_cast<const f4*>(vec + cw);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int wi = tg * 16 + 4 * lg + r;
+          const int o = COL ? si - wi : wi - si;  // j - i
+          float x = __builtin_fmaf(sacc[r], g.scale2, w4[r] + sbias);
+          x = (o >= -g.h1 && o <= g.h2 && sok && wi >= 0 && wi < n) ? x : kNegInf;
+          const float pe = exp2_fast(x);
+          if (MODE == 0) {
+            val[tt][r] = pe * z4[r];
+          } else if (MODE == 2) {
+            val[tt][r] = pe;
+          } else {
+            float br = dacc[r];
+#pragma unroll
+            for (int k = 0; k < kMaxR; ++k) {
+              if (k < R) {
+                const float m0 = vec[(size_t)(2 * k) * NWC + cw + r];
+                const float m1 = vec[(size_t)(2 * k + 1) * NWC + cw + r];
+                br -= COL ? m0 * sm0[k] : sm0[k] * m0;
+                br -= COL ? m1 * sm1[k] : sm1[k] * m1;
+              }
+            }
+            val[tt][r] = pe * br;
+          }
+        }
+      }
+    }
+    if (MODE == 0) {
+      vacc += (val[0][0] + val[0][1]) + (val[0][2] + val[0][3]);
+      vacc += (val[1][0] + val[1][1]) + (val[1][2] + val[1][3]);
+    } else if (any) {
+      u4 hi, lo;
+      split_hilo(val[0], val[1], hi, lo);
+      const char* pb = tbuf + (size_t)(buf * NTEN + PT) * TBYTES;
+#pragma unroll
+      for (int ds = 0; ds < ND; ++ds) {
+        const u2 b0 = ld_tr16(pb + offB[ds]);
+        const u2 b1 = ld_tr16(pb + 16 * RB + offB[ds]);
+        const u4 bv = {b0.x, b0.y, b1.x, b1.y};
+        acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], hi, bv);
+        acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], lo, bv);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!wactive) return;
+  if (MODE == 0) {
+    const float tot = cross_row_sum(vacc);
+    if (lg == 0 && sok) {
+      if (!COL) {
+        const int i = si;
+        float a2 = tot;
+        if (g.dustbin) {
+          // entry (i, delta): P_i,delta z_delta
+          const double vRd = p.tail_v[slot(R, BHL) + bh * L + n];
+          const float zd = exp2f(p.tail_v[slot(p.r, BHL) + bh * L + n] - vRd) *
+                           p.vbar[slot(p.r, BHL) + bh * L + n] / p.b[(size_t)bb * L + n];
+          a2 += exp2f(p.sdc[bh * L + i] + uR[i] + vRd) * zd;
+        }
+        const float alpha = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + i] - uR[i]);
+        const float ub = (p.r == R ? p.D[bh * L + i] : 0.f) - alpha * a2;
+        p.x[slot(p.r, BHL) + bh * L + i] = ub / p.a[(size_t)bb * L + i];
+      } else {
+        const int j = si;
+        float a2 = tot;
+        if (g.dustbin) {
+          // entry (delta, j): P_delta,j zz_delta
+          const double uRd = p.tail_u[slot(R, BHL) + bh * L + n];
+          const float zd = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + n] - uRd) * p.x[slot(p.r, BHL) + bh * L + n];
+          a2 += exp2f(p.sdr[bh * L + j] + uRd + vR[j]) * zd;
+        }
+        const float beta = exp2f(p.tail_v[slot(p.r - 1, BHL) + bh * L + j] - vR[j]);
+        p.vbar[slot(p.r - 1, BHL) + bh * L + j] = -beta * a2;
+      }
+    }
+  } else {
+    const float sc = MODE == 1 ? g.inv_sqrt_d : 1.f;
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = sidx0 + 4 * lg + r;
+        if (s < n) p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = acc[ds][r] * sc;
+      }
+    }
+  }
+}
+
 template <typename T, int D>
 static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspace& w, hipStream_t st) {
   constexpr int EB = Elt<T>::kBytes;
@@ -820,29 +1174,66 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   if (g.dustbin) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
   const dim3 tok((g.L + kTokPerBlock - 1) / kTokPerBlock, nbh);
   hipLaunchKernelGGL(bw_rowdot<T>, tok, dim3(256), 0, st, g, dOt, f.O, Dv);
+  // bf16 with d >= 64: streamed sweeps (one workgroup per 128-index block)
+  constexpr bool kSweep = sizeof(T) == 2 && D >= 64;
+  const int sgrid = (nbh * ceil_div_pos(g.L, 128) + 7) & ~7;
+  BwArgs ps = p;
+  ps.padded_grid = sgrid;
+  auto sweep_lds = [&](bool col, int mode) {
+    const int NT = col ? g.NTc : g.NT;
+    const int NP = (NT + kSwWaves) / 2;
+    const int NWC = 2 * NP * 16;
+    const int ntens = mode == 0 ? 1 : 2;
+    const int nv = mode == 0 ? 1 : (mode == 1 ? 2 * R : 0);
+    return (size_t)2 * ntens * 32 * D * 2 + (size_t)NWC * 4 * (1 + nv) + 64;
+  };
+  if constexpr (kSweep) {
+#define SET_SW(COLV, MODEV)                                                                                     err = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV>),                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds(COLV, MODEV));           if (err != hipSuccess) return err;
+    SET_SW(false, 0) SET_SW(false, 1) SET_SW(true, 0) SET_SW(true, 1) SET_SW(true, 2)
+#undef SET_SW
+  }
   // dV (band) -> add dustbin row, E, vbar^(R)
   p.out = f.dV;
-  hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
+  ps.out = f.dV;
+  if constexpr (kSweep)
+    hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
+  else
+    hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
   hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, w.tail_u, w.tail_v, w.sdr, R, f.dV,
                      vbar + (size_t)R * BHL);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
   // adjoint vectors through the tail
   for (int r = R; r >= 1; --r) {
     p.r = r;
-    hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
+    ps.r = r;
+    if constexpr (kSweep)
+      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 0>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 0), st, g, ps);
+    else
+      hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
     if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 1);
     if (r > 1 || f.vbar0) {
-      hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
+      if constexpr (kSweep)
+        hipLaunchKernelGGL((bw_sweep_kernel<D, true, 0>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 0), st, g, ps);
+      else
+        hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
       if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 2);
     }
   }
   // dQ, dK
   p.out = f.dQ;
-  hipLaunchKernelGGL((bw_row_kernel<T, D, 1>), dim3(grid), dim3(256), row_grad_lds, st, g, p);
+  ps.out = f.dQ;
+  if constexpr (kSweep)
+    hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st, g, ps);
+  else
+    hipLaunchKernelGGL((bw_row_kernel<T, D, 1>), dim3(grid), dim3(256), row_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 0>), tg, dim3(256), 0, st, g, p);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 3);
   p.out = f.dK;
-  hipLaunchKernelGGL((bw_col_kernel<T, D, 1>), dim3(grid), dim3(256), col_grad_lds, st, g, p);
+  ps.out = f.dK;
+  if constexpr (kSweep)
+    hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st, g, ps);
+  else
+    hipLaunchKernelGGL((bw_col_kernel<T, D, 1>), dim3(grid), dim3(256), col_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 1>), tg, dim3(256), 0, st, g, p);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 4);
   if (f.vbar0) hipLaunchKernelGGL(bw_copy_vbar0, tg, dim3(256), 0, st, g, vbar, f.vbar0);

@@ -84,6 +84,30 @@ def test_dustbin_config():
     _check(workloads.make(4), TOL_F32)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_dustbin_bf16_ragged(d):
+    """bf16 with a dustbin and ragged lengths: the streamed backward sweeps
+    (d >= 64) with the dustbin terms of the adjoint vector passes."""
+    prob = workloads.custom(B=2, H=2, L=400, d=d, W=96, T=12, R=2, dtype="bf16",
+                            lengths=[399, 250], dustbin=True, seed=11, name=f"dustbin-bf16-d{d}")
+    _check(prob, TOL_BF16)
+
+
+def test_bf16_vbar0_and_tail_r3():
+    """bf16, d = 128, R = 3 with vbar0 requested (the last column pass)."""
+    prob = workloads.custom(B=1, H=2, L=300, d=128, W=64, T=5, R=3, dtype="bf16", seed=5,
+                            name="bf16-R3")
+    gpu = run_gpu(prob, want_vbar0=True)
+    ref = run_oracle(prob)
+    errs = compare(gpu, ref, prob)
+    log("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL_BF16[k], (k, v)
+    from tests.gpu_util import rel_err, active_mask
+    act = np.broadcast_to(active_mask(prob)[:, None, :], gpu["u"].shape)
+    assert rel_err(gpu["vbar0"], ref["vbar0"], act) < 1e-3
+
+
 def test_dustbin_vbar0_and_tail_stack():
     prob = workloads.custom(B=2, H=2, L=96, d=32, W=20, T=6, R=2, lengths=[70, 81],
                             dustbin=True, seed=3)
