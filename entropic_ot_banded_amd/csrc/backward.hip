@@ -817,8 +817,8 @@ __device__ __forceinline__ void split_hilo(const float (&v0)[4], const float (&v
   lo = (u4){lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
 }
 
-template <int D, bool COL, int MODE>
-__global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) {
+template <int D, bool COL, int MODE, int RM>
+__global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(Geom g, BwArgs p) {
   constexpr int RB = D * 2;           // bytes per row (bf16)
   constexpr int CPR = RB / 16;        // 16-byte chunks per row
   constexpr int NCH = RB / 64;        // 32-element MFMA chunks per row
@@ -949,9 +949,9 @@ __global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) 
   }
   // strip-side exponent part and strip modifiers (MODE 1)
   const float sbias = sok ? (float)((COL ? vR[si] : uR[si]) + ref) : 0.f;
-  float sm0[kMaxR], sm1[kMaxR];
+  float sm0[RM], sm1[RM];  // RM >= R: tail depth bound of this instance
 #pragma unroll
-  for (int k = 0; k < kMaxR; ++k) {
+  for (int k = 0; k < RM; ++k) {
     sm0[k] = 0.f;
     sm1[k] = 0.f;
     if (MODE == 1 && k < R && sok) {
@@ -966,17 +966,22 @@ __global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) 
     }
   }
 
-  // per-lane LDS offsets: A-operand chunks of row lr; transposed B reads
-  int offA[NCH];
+  // per-lane LDS offsets: A-operand chunks of row lr; transposed B reads.
+  // The swizzle only touches the low 3 bits of a chunk index, so chunks 8
+  // apart are 128 bytes apart: two (resp. four) bases cover all of them.
+  int offA2[2];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) offA[c] = lr * RB + sw_chunk(4 * c + lg, lr) * 16;
-  int offB[ND];
+  for (int c = 0; c < 2; ++c) offA2[c] = lr * RB + sw_chunk(4 * c + lg, lr) * 16;
+  auto offA = [&](int c) { return offA2[c & 1] + (c >> 1) * 128; };
+  constexpr int NB = ND < 4 ? ND : 4;
+  int offB4[NB];
   {
     const int m = lr;  // lane within its 16-lane group; group = lg
     const int row = 4 * lg + (m >> 2);
 #pragma unroll
-    for (int ds = 0; ds < ND; ++ds) offB[ds] = row * RB + sw_chunk(2 * ds + ((m & 3) >> 1), row) * 16 + 8 * (m & 1);
+    for (int ds = 0; ds < NB; ++ds) offB4[ds] = row * RB + sw_chunk(2 * ds + ((m & 3) >> 1), row) * 16 + 8 * (m & 1);
   }
+  auto offB = [&](int ds) { return offB4[ds & 3] + (ds >> 2) * 128; };
 
   float vacc = 0.f;  // MODE 0
   f4 acc[ND];
@@ -1014,14 +1019,14 @@ __global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) 
         f4 sacc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const u4 a = ld16(tb0 + offA[c]);
+          const u4 a = ld16(tb0 + offA(c));
           sacc = Elt<bf16_t>::mma_chunk(sacc, a, sb0[c]);
         }
         if (MODE == 1) {
           const char* tb1 = tbuf + (size_t)(buf * NTEN + 1) * TBYTES + tt * 16 * RB;
 #pragma unroll
           for (int c = 0; c < NCH; ++c) {
-            const u4 a = ld16(tb1 + offA[c]);
+            const u4 a = ld16(tb1 + offA(c));
             dacc = Elt<bf16_t>::mma_chunk(dacc, a, sb1[c]);
           }
         }
@@ -1044,7 +1049,7 @@ __global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) 
           } else {
             float br = dacc[r];
 #pragma unroll
-            for (int k = 0; k < kMaxR; ++k) {
+            for (int k = 0; k < RM; ++k) {
               if (k < R) {
                 const float m0 = vec[(size_t)(2 * k) * NWC + cw + r];
                 const float m1 = vec[(size_t)(2 * k + 1) * NWC + cw + r];
@@ -1066,8 +1071,8 @@ __global__ __launch_bounds__(kSwThreads) void bw_sweep_kernel(Geom g, BwArgs p) 
       const char* pb = tbuf + (size_t)(buf * NTEN + PT) * TBYTES;
 #pragma unroll
       for (int ds = 0; ds < ND; ++ds) {
-        const u2 b0 = ld_tr16(pb + offB[ds]);
-        const u2 b1 = ld_tr16(pb + 16 * RB + offB[ds]);
+        const u2 b0 = ld_tr16(pb + offB(ds));
+        const u2 b1 = ld_tr16(pb + 16 * RB + offB(ds));
         const u4 bv = {b0.x, b0.y, b1.x, b1.y};
         acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], hi, bv);
         acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], lo, bv);
@@ -1188,15 +1193,19 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     return (size_t)2 * ntens * 32 * D * 2 + (size_t)NWC * 4 * (1 + nv) + 64;
   };
   if constexpr (kSweep) {
-#define SET_SW(COLV, MODEV)                                                                                     err = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV>),                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds(COLV, MODEV));           if (err != hipSuccess) return err;
-    SET_SW(false, 0) SET_SW(false, 1) SET_SW(true, 0) SET_SW(true, 1) SET_SW(true, 2)
+#define SET_SW(COLV, MODEV, RMV)                                                                        \
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV, RMV>),        \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds(COLV, MODEV));   \
+  if (err != hipSuccess) return err;
+    SET_SW(false, 0, 2) SET_SW(false, 1, 2) SET_SW(true, 0, 2) SET_SW(true, 1, 2) SET_SW(true, 2, 2)
+    SET_SW(false, 1, kMaxR) SET_SW(true, 1, kMaxR)
 #undef SET_SW
   }
   // dV (band) -> add dustbin row, E, vbar^(R)
   p.out = f.dV;
   ps.out = f.dV;
   if constexpr (kSweep)
-    hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
+    hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
   else
     hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
   hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, w.tail_u, w.tail_v, w.sdr, R, f.dV,
@@ -1207,13 +1216,13 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     p.r = r;
     ps.r = r;
     if constexpr (kSweep)
-      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 0>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 0), st, g, ps);
+      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 0), st, g, ps);
     else
       hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
     if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 1);
     if (r > 1 || f.vbar0) {
       if constexpr (kSweep)
-        hipLaunchKernelGGL((bw_sweep_kernel<D, true, 0>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 0), st, g, ps);
+        hipLaunchKernelGGL((bw_sweep_kernel<D, true, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 0), st, g, ps);
       else
         hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
       if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 2);
@@ -1222,16 +1231,26 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   // dQ, dK
   p.out = f.dQ;
   ps.out = f.dQ;
-  if constexpr (kSweep)
-    hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st, g, ps);
+  if constexpr (kSweep) {
+    if (R <= 2)
+      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st, g, ps);
+    else
+      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1, kMaxR>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st, g,
+                         ps);
+  }
   else
     hipLaunchKernelGGL((bw_row_kernel<T, D, 1>), dim3(grid), dim3(256), row_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 0>), tg, dim3(256), 0, st, g, p);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 3);
   p.out = f.dK;
   ps.out = f.dK;
-  if constexpr (kSweep)
-    hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st, g, ps);
+  if constexpr (kSweep) {
+    if (R <= 2)
+      hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st, g, ps);
+    else
+      hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1, kMaxR>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st, g,
+                         ps);
+  }
   else
     hipLaunchKernelGGL((bw_col_kernel<T, D, 1>), dim3(grid), dim3(256), col_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 1>), tg, dim3(256), 0, st, g, p);
