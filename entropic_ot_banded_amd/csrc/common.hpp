@@ -146,6 +146,39 @@ __device__ __forceinline__ float wave_max(float x) { return cross_row_max(row16_
 __device__ __forceinline__ u4 ld16(const void* p) { return *reinterpret_cast<const u4*>(p); }
 __device__ __forceinline__ void st16(void* p, u4 v) { *reinterpret_cast<u4*>(p) = v; }
 
+// ---------------------------------------------------------------------------
+// Streamed tile pairs in LDS (bf16 rows of RB >= 128 bytes).
+// A stored row swizzles its 16-byte chunks: chunk c of row r sits at
+// position c ^ f(r & 7), f = (r & 3) << 1 | (r >> 2) & 1, so 128-bit reads of
+// 8 consecutive rows and transposed 64-bit reads of 4 consecutive rows (the
+// two access patterns of the MFMA operands below) hit distinct banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int sw_chunk(int chunk, int row) {
+  return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+}
+
+__device__ __forceinline__ u2 ld_tr16(const char* p) {
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p));
+  u2 r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
+// hi + lo bf16 operands of 8 fp32 values (4 of tile 0, then 4 of tile 1)
+__device__ __forceinline__ void split_hilo(const float (&v0)[4], const float (&v1)[4], u4& hi, u4& lo) {
+  uint32_t hb[8], lb[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hb[r] = float_to_bf16_bits(v0[r]);
+    hb[4 + r] = float_to_bf16_bits(v1[r]);
+    lb[r] = float_to_bf16_bits(v0[r] - bits_to_float(hb[r] << 16));
+    lb[4 + r] = float_to_bf16_bits(v1[r] - bits_to_float(hb[4 + r] << 16));
+  }
+  hi = (u4){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+  lo = (u4){lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+}
+
 // Map a linear workgroup id to a logical one so that each XCD (ids are dealt
 // to the 8 XCDs round-robin) receives a contiguous range of logical ids:
 // neighbouring band blocks then share that XCD's L2.  `padded` is the launch

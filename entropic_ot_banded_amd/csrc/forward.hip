@@ -1018,6 +1018,223 @@ __global__ __launch_bounds__(512) void output_kernel(Geom g, OutArgs p) {
   }
 }
 
+// Output epilogue for bf16 with d >= 64: the same results as output_kernel,
+// with the band tiles streamed through LDS as in the backward sweeps.  One
+// workgroup of 8 waves per 128-row block; the block's NT + 7 window tiles of
+// K (score side, MFMA A operand) and V (product side) pass through LDS two at
+// a time, double-buffered; a wave keeps its 16-row Q strip and its O tile in
+// registers.  P enters the P V product as hi + lo bf16 (4 + 4 k-slots per
+// lane over the tile pair) against V rows read transposed from LDS.
+template <int D>
+__global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
+  constexpr int RB = D * 2;
+  constexpr int CPR = RB / 16;
+  constexpr int NCH = RB / 64;
+  constexpr int ND = D / 16;
+  constexpr int TBYTES = 32 * RB;
+  constexpr int kThreads = 512;
+  static_assert(CPR >= 8, "the chunk swizzle needs 8 chunks per row");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ double sh_vref;
+
+  const int nbh = g.B * g.H;
+  const int logical = xcd_remap(blockIdx.x, p.padded_grid);
+  if (logical >= nbh * g.nblk) return;
+  const int bh = logical / g.nblk;
+  const int blk = logical - bh * g.nblk;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const int r0 = blk * kBlockRows;
+  const size_t L = g.L;
+  const int tid = threadIdx.x;
+  const double ln2 = 0.6931471805599453;
+
+  // u outputs, filler rows of u, v and O for the owned range
+  for (int c = tid; c < kBlockRows; c += kThreads) {
+    const int i = r0 + c;
+    if (i >= g.L) break;
+    if (i >= n) {
+      if (!(g.dustbin && i == n)) {
+        p.u_out[bh * L + i] = kNegInf;
+        p.v_out[bh * L + i] = kNegInf;
+      }
+    } else {
+      p.u_out[bh * L + i] = p.u_in ? (float)(p.u_in[bh * L + i] * ln2) : 0.f;
+    }
+  }
+  for (int idx = tid; idx < kBlockRows * D; idx += kThreads) {
+    const int i = r0 + idx / D;
+    if (i < g.L && i >= n && !(g.dustbin && i == n)) p.O[(bh * L + i) * D + idx % D] = 0.f;
+  }
+  if (r0 >= n) return;
+
+  const int NT = g.NT;
+  const int NW = NT + kWaves - 1;
+  const int NP = (NW + 1) >> 1;
+  const int NWC = 2 * NP * 16;
+  const int tw0 = blk * 8 - g.TL;
+  char* tbuf = smem;                                        // [2][2 tensors][32 rows][RB]
+  float* wv = reinterpret_cast<float*>(smem + 4 * TBYTES);  // [NWC] v_j - vref
+
+  if (tid == 0)
+    sh_vref = p.part_in ? finish_v(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr) : 0.0;
+  __syncthreads();
+  const double vref = sh_vref;
+  for (int c = tid; c < NWC; c += kThreads) {
+    const int j = tw0 * 16 + c;
+    float w = kNegInf;
+    if (j >= 0 && j < n) {
+      double vj = 0.0;
+      if (p.part_in) vj = finish_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
+      if (j >= r0 && j < r0 + kBlockRows) {
+        p.v_out[bh * L + j] = (float)(vj * ln2);
+        if (p.v_tail) p.v_tail[bh * L + j] = vj;
+      }
+      w = (float)(vj - vref);
+    }
+    wv[c] = w;
+  }
+
+  const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
+  const char* Vb = reinterpret_cast<const char*>(p.V) + (size_t)bh * L * RB;
+  u4 pre[2];
+  int pre_row = 0;
+  auto load_pair = [&](int pp) {
+    const int r32 = tid / CPR;
+    int grow = (tw0 + 2 * pp) * 16 + r32;
+    pre_row = grow;
+    grow = grow < 0 ? 0 : (grow >= (int)L ? (int)L - 1 : grow);
+    if (tid < 32 * CPR) {
+      pre[0] = ld16(Kb + (size_t)grow * RB + (tid % CPR) * 16);
+      pre[1] = ld16(Vb + (size_t)grow * RB + (tid % CPR) * 16);
+    }
+  };
+  auto store_pair = [&](int buf) {
+    if (tid < 32 * CPR) {
+      const int r32 = tid / CPR, c16 = tid % CPR;
+      const bool ok = pre_row >= 0 && pre_row < n;
+      const int off = r32 * RB + sw_chunk(c16, r32) * 16;
+#pragma unroll
+      for (int te = 0; te < 2; ++te)
+        st16(tbuf + (size_t)(buf * 2 + te) * TBYTES + off, ok ? pre[te] : (u4){0u, 0u, 0u, 0u});
+    }
+  };
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int i0 = r0 + wave * 16;
+  const int si = i0 + lr;
+  const bool sok = si < n;
+  const int sic = si < (int)L ? si : (int)L - 1;
+  const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
+  u4 qs[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u4 q = ld16(Qb + (size_t)sic * RB + c * 64 + lg * 16);
+    qs[c] = sok ? q : (u4){0u, 0u, 0u, 0u};
+  }
+  const float ui2 = sok ? (float)((p.u_in ? p.u_in[bh * L + si] : 0.0) + vref) : 0.f;
+
+  int offA2[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) offA2[c] = lr * RB + sw_chunk(4 * c + lg, lr) * 16;
+  constexpr int NB = ND < 4 ? ND : 4;
+  int offB4[NB];
+  {
+    const int row = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int ds = 0; ds < NB; ++ds) offB4[ds] = row * RB + sw_chunk(2 * ds + ((lr & 3) >> 1), row) * 16 + 8 * (lr & 1);
+  }
+
+  f4 oacc[ND];
+#pragma unroll
+  for (int ds = 0; ds < ND; ++ds) oacc[ds] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  load_pair(0);
+  store_pair(0);
+  if (NP > 1) load_pair(1);
+  __syncthreads();
+  const bool wactive = i0 < n;
+  for (int pp = 0; pp < NP; ++pp) {
+    const int buf = pp & 1;
+    if (pp + 1 < NP) {
+      store_pair(buf ^ 1);
+      if (pp + 2 < NP) load_pair(pp + 2);
+    }
+    float val[2][4];
+    bool any = false;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int wt = 2 * pp + tt;
+      const int t = wt - wave;
+      const int tg = tw0 + wt;
+      const bool act = wactive && t >= 0 && t < NT && tg >= 0 && tg * 16 < n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) val[tt][r] = 0.f;
+      if (act) {
+        any = true;
+        const char* tb0 = tbuf + (size_t)(buf * 2) * TBYTES + tt * 16 * RB;
+        f4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const u4 a = ld16(tb0 + offA2[c & 1] + (c >> 1) * 128);
+          sacc = Elt<bf16_t>::mma_chunk(sacc, a, qs[c]);
+        }
+        const int cw = wt * 16 + 4 * lg;
+        const f4 w4 = *reinterpret_cast<const f4*>(wv + cw);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int wj = tg * 16 + 4 * lg + r;
+          const int o = wj - si;
+          float x = __builtin_fmaf(sacc[r], g.scale2, w4[r] + ui2);
+          x = (o >= -g.h1 && o <= g.h2 && sok && wj >= 0 && wj < n) ? x : kNegInf;
+          val[tt][r] = exp2_fast(x);
+        }
+      }
+    }
+    if (any) {
+      u4 hi, lo;
+      split_hilo(val[0], val[1], hi, lo);
+      const char* pb = tbuf + (size_t)(buf * 2 + 1) * TBYTES;
+#pragma unroll
+      for (int ds = 0; ds < ND; ++ds) {
+        const int ob = offB4[ds & 3] + (ds >> 2) * 128;
+        const u2 b0 = ld_tr16(pb + ob);
+        const u2 b1 = ld_tr16(pb + 16 * RB + ob);
+        const u4 bv = {b0.x, b0.y, b1.x, b1.y};
+        oacc[ds] = Elt<bf16_t>::mma_chunk(oacc[ds], hi, bv);
+        oacc[ds] = Elt<bf16_t>::mma_chunk(oacc[ds], lo, bv);
+      }
+    }
+    __syncthreads();
+  }
+  if (!wactive) return;
+  // dustbin column term for real rows: P_i,delta V_delta
+  float pd[4] = {0.f, 0.f, 0.f, 0.f};
+  if (g.dustbin) {
+    const double vd = p.dstate ? p.dstate[4 * bh + 1] : 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * lg + r;
+      if (i < n) {
+        const double ui = p.u_in ? p.u_in[bh * L + i] : 0.0;
+        pd[r] = exp2_fast((float)((double)p.sdc[bh * L + i] + ui + vd));
+      }
+    }
+  }
+  const bf16_t* Vbase = reinterpret_cast<const bf16_t*>(p.V) + ((size_t)bh * L + (g.dustbin ? n : 0)) * D;
+#pragma unroll
+  for (int ds = 0; ds < ND; ++ds) {
+    const int col = ds * 16 + lr;
+    const float vdel = g.dustbin ? Elt<bf16_t>::load(Vbase, col) : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * lg + r;
+      if (i < n) p.O[((size_t)bh * L + i) * D + col] = oacc[ds][r] + pd[r] * vdel;
+    }
+  }
+}
+
 // Dustbin row of the output: O_delta = sum_j P_delta,j V_j over active j,
 // plus u, v of the dustbin (state fp64 log2 units, outputs natural).
 // One workgroup per (b, h); thread c owns column c of the head dimension.
@@ -1149,7 +1366,16 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   o.v_out = f.v;
   o.v_tail = w.tail_v + (size_t)f.R * BHL;
   o.padded_grid = grid;
-  hipLaunchKernelGGL((output_kernel<T, D>), dim3(grid), dim3(512), out_lds, st, g, o);
+  if constexpr (sizeof(T) == 2 && D >= 64) {
+    const int NP = (g.NT + kWaves) / 2;
+    const size_t sweep_lds = (size_t)4 * 32 * D * 2 + (size_t)2 * NP * 16 * 4 + 64;
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(output_sweep_kernel<D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((output_sweep_kernel<D>), dim3(grid), dim3(512), sweep_lds, st, g, o);
+  } else {
+    hipLaunchKernelGGL((output_kernel<T, D>), dim3(grid), dim3(512), out_lds, st, g, o);
+  }
   if (g.dustbin) {
     hipLaunchKernelGGL(dustbin_output<T>, dim3(nbh), dim3(128), 0, st, g, reinterpret_cast<const T*>(f.V),
                        w.tail_v + (size_t)f.R * BHL, o.dstate, w.sdr, f.O, f.u, f.v);
