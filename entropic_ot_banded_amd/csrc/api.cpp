@@ -75,6 +75,8 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
   x.TRc = (15 + h1) / 16;
   x.NTc = x.TLc + x.TRc + 1;
   if (x.TL + (15 + h2) / 16 + 1 > kMaxTiles || x.NTc > kMaxTiles) return SINKATTN_EUNSUPPORTED;
+  // per-(b, h) slices are addressed with 32-bit byte offsets
+  if ((long long)s->L * s->d * (s->dtype == SINKATTN_BF16 ? 2 : 4) >= (1ll << 31)) return SINKATTN_EUNSUPPORTED;
   x.nblk = (s->L + kBlockRows - 1) / kBlockRows;
   x.NWC = 16 * (x.TL + x.TR + kWaves);
   // Segments: a workgroup sweeps SB consecutive blocks so the K window slides

@@ -314,18 +314,19 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   };
   // Loads are unconditional from row indices clamped into [0, L): rows past
   // the sequence only feed entries that the strip masks (rowok).
+  const float* a_b = p.a + (size_t)bb * L;   // per-sequence / per-(b, h) bases
+  const float* sdc_bh = p.sdc + (size_t)bh * L;
   auto load_q_chunk = [&](int k, int c, RowIn& ri) {
-    int qi = k * kBlockRows + wave * 16 + lr;
-    qi = qi < (int)L ? qi : (int)L - 1;
-    ri.q[c] = ld16(Qb + (size_t)qi * RB + c * 64 + lg * 16);
+    const int qi = min(k * kBlockRows + wave * 16 + lr, (int)L - 1);
+    ri.q[c] = ld16(Qb + (uint32_t)(qi * RB + c * 64 + lg * 16));
   };
   auto load_row_scalars = [&](int k, RowIn& ri) {
     const int ib = k * kBlockRows + wave * 16 + 4 * lg;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = ib + r < (int)L ? ib + r : (int)L - 1;
-      ri.a[r] = p.a[(size_t)bb * L + i];
-      ri.sd[r] = p.sdc[bh * L + i];  // always allocated; used only with a dustbin
+      const uint32_t i = (uint32_t)min(ib + r, (int)L - 1);
+      ri.a[r] = a_b[i];
+      ri.sd[r] = sdc_bh[i];  // always allocated; used only with a dustbin
     }
   };
   RowIn cur;
@@ -396,10 +397,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     auto prefetch = [&](int part) {
       if (part < NEWLD) {
         // rows past the sequence are zeroed when stored to LDS
+        // (a per-(b, h) base pointer plus a 32-bit lane offset: the load
+        // takes the scalar base directly, no 64-bit address arithmetic)
         const int idx = tid + part * kThreads;
-        int j = jp0 + idx / PER_ROW;
-        j = j < (int)L ? j : (int)L - 1;
-        knew[part] = ld16(Kb + (size_t)j * RB + (idx % PER_ROW) * 16);
+        const int j = min(jp0 + idx / PER_ROW, (int)L - 1);
+        knew[part] = ld16(Kb + (uint32_t)(j * RB + (idx % PER_ROW) * 16));
       } else if (part < NEWLD + NCH) {
         load_q_chunk(kn, part - NEWLD, nxt);
       } else if (part == NEWLD + NCH) {
