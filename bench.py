@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSV output")
+    ap.add_argument("--converge-tol", type=float, default=5e-5,
+                    help="also time the early-stopping base at this tolerance (0: skip)")
+    ap.add_argument("--converge-every", type=int, default=5)
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
@@ -326,6 +329,29 @@ def main():
     torch.cuda.synchronize()
     fwd_ms, bwd_ms = fb[0].elapsed_time(fb[1]), fb[1].elapsed_time(fb[2])
 
+    # The convergence-controlled base on the same inputs, T as its cap
+    # (sinkattn_forward_converge; host-timed, since it waits at each check).
+    converged = None
+    if args.converge_tol > 0:
+        def conv_step():
+            O, u, v, wsc, T_used, err_last = eoba.forward_converge(
+                Q, K, V, W, T, R, a, b, args.converge_tol, args.converge_every, workspace=ws)
+            eoba.backward(Q, K, V, W, T_used, R, a, b, O, dO, wsc)
+            return T_used, err_last
+        conv_step()
+        times = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            c0 = time.perf_counter()
+            T_used, err_last = conv_step()
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - c0)
+        c_ms = sorted(times)[len(times) // 2] * 1e3
+        converged = {"tol": args.converge_tol, "check_every": args.converge_every, "T_max": T,
+                     "T_used": T_used, "err_last": err_last, "ms_per_step": round(c_ms, 4),
+                     "tokens_per_s": round(prob.real_tokens() / (c_ms * 1e-3), 1),
+                     "timing": "host clock, median of 5 forward_converge + backward"}
+
     if args.copy_calibration:
         x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         y = torch.empty_like(x)
@@ -371,6 +397,8 @@ def main():
                       "inputs": "bf16", "accumulate": "fp32", "state": "fp64"},
            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "wall_s": round(wall, 3),
            "roofline": roofline, "path_roofline": path}
+    if converged is not None:
+        out["converged_base"] = converged
     if not args.no_cpu_baseline:
         cb = cpu_baseline(prob, args.cpu_heads)
         cb.pop("seconds", None)

@@ -25,7 +25,7 @@ SINKATTN_F32 = 0
 SINKATTN_BF16 = 1
 
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
-            "sinkattn_backward", "sinkattn_timing_enable", "sinkattn_timing_collect",
+            "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_timing_enable", "sinkattn_timing_collect",
             "sinkattn_status_string", "sinkattn_version")
 
 
@@ -62,6 +62,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_tail_offset.restype = sz
     lib.sinkattn_forward.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, vp, sz, vp]
     lib.sinkattn_forward.restype = i32
+    lib.sinkattn_forward_converge.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, ctypes.c_double,
+                                              i32, vp, vp, vp, vp, sz, ctypes.POINTER(i32),
+                                              ctypes.POINTER(ctypes.c_double), vp]
+    lib.sinkattn_forward_converge.restype = i32
     lib.sinkattn_backward.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, sz,
                                       vp, vp, vp, vp, vp]
     lib.sinkattn_backward.restype = i32
@@ -206,6 +210,38 @@ def forward(Q, K, V, W: int, T: int, R: int, a, b, lengths=None, dustbin: bool =
         _ptr(v), _ptr(workspace), workspace.numel(), _stream(Q.device))
     _check(st)
     return O, u, v, workspace
+
+
+def forward_converge(Q, K, V, W: int, T_max: int, R: int, a, b, tol: float, check_every: int = 1,
+                     lengths=None, dustbin: bool = False, workspace=None):
+    """Forward pass whose stopped base ends once every (b, h) problem's L1
+    row-marginal error is below `tol` (checked every `check_every` steps, at
+    most T_max steps; R >= 1).  Blocks at each check.  Returns
+    (O, u, v, workspace, T_used, err_last); pass T_used to `backward`.
+    err_last is the largest per-problem error at the last check (None if no
+    check ran)."""
+    torch = _torch()
+    _validate(Q, K, V, a, b, lengths)
+    shape = _shape_of(Q, lengths, dustbin)
+    nbytes = workspace_bytes(shape, W, R)
+    if nbytes == 0:
+        raise SinkattnError(SINKATTN_EINVAL, "invalid shape/W/R")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    B, H, L, d = Q.shape
+    O = torch.empty((B, H, L, d), dtype=torch.float32, device=Q.device)
+    u = torch.empty((B, H, L), dtype=torch.float32, device=Q.device)
+    v = torch.empty((B, H, L), dtype=torch.float32, device=Q.device)
+    s = shape.c()
+    t_used = ctypes.c_int32(-1)
+    err = ctypes.c_double(float("-inf"))  # untouched when no check runs
+    st = load_library().sinkattn_forward_converge(
+        _ptr(Q), _ptr(K), _ptr(V), W, T_max, R, _ptr(a), _ptr(b), ctypes.byref(s), float(tol),
+        int(check_every), _ptr(O), _ptr(u), _ptr(v), _ptr(workspace), workspace.numel(),
+        ctypes.byref(t_used), ctypes.byref(err), _stream(Q.device))
+    _check(st)
+    err_last = None if err.value == float("-inf") else err.value
+    return O, u, v, workspace, t_used.value, err_last
 
 
 def backward(Q, K, V, W: int, T: int, R: int, a, b, O, dO, workspace, lengths=None,

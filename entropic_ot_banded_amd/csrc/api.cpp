@@ -218,6 +218,29 @@ int sinkattn_forward(const void* Q, const void* K, const void* V, int W, int T, 
   return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
 }
 
+int sinkattn_forward_converge(const void* Q, const void* K, const void* V, int W, int T_max, int R,
+                              const float* a, const float* b, const sinkattn_shape* s, double tol,
+                              int check_every, float* O, float* u, float* v, void* workspace,
+                              size_t workspace_bytes, int* T_used, double* err_last, hipStream_t stream) {
+  if (!Q || !K || !V || !a || !b || !O || !u || !v || !workspace || !T_used) return SINKATTN_EINVAL;
+  if (T_max < 0 || R < 1 || check_every < 1 || !(tol >= 0.0)) return SINKATTN_EINVAL;
+  Geom g;
+  int st = make_geom(s, W, &g);
+  if (st != SINKATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+    return SINKATTN_EINVAL;
+  Workspace w = carve(static_cast<float*>(workspace), g, R);
+  if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
+  FwdLaunch f{Q, K, V, a, b, O, u, v, T_max, R};
+  f.stop.every = check_every;
+  f.stop.tol = tol;
+  f.stop.T_used = T_used;
+  f.stop.err_last = err_last;
+  hipError_t e = launch_forward(g, s->dtype, f, w, stream);
+  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
+  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+}
+
 int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T, int R, const float* a,
                       const float* b, const sinkattn_shape* s, const float* O, const void* dO, void* workspace,
                       size_t workspace_bytes, float* dQ, float* dK, float* dV, float* vbar0,

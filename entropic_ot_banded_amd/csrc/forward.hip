@@ -31,6 +31,9 @@
 // direction (u + c, v - c) by about one ulp of |log b| per step.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+#include <vector>
+
 #include "common.hpp"
 #include "geom.hpp"
 
@@ -690,6 +693,7 @@ struct DustArgs {
   double* u_tail;       // optional: u^(t) slot
   double* v_tail;       // optional: v^(t) slot
   double* u_out;        // latest-u buffer (dustbin entry)
+  double* v_prev_tail;  // optional: copy of v^(t-1)_delta (the state this step starts from)
   int first;
 };
 
@@ -702,6 +706,7 @@ __global__ __launch_bounds__(256) void dustbin_step(Geom g, DustArgs p) {
   __shared__ double redd[256];
   __shared__ float red[256];
   const double vd_prev = p.first ? 0.0 : p.dstate[4 * bh + 1];
+  if (p.v_prev_tail && tid == 0) p.v_prev_tail[bh * L + n] = vd_prev;
   const float* srow = p.sdr + bh * L;
   // x_j = S_delta,j + v_j (log2) over active j; the corner uses v_delta
   double m = -__builtin_inf();
@@ -780,6 +785,43 @@ __global__ void zero_start(Geom g, double* tail_u0, double* tail_v0) {
   const size_t o = (size_t)bh * g.L + i;
   tail_u0[o] = 0.0;
   tail_v0[o] = 0.0;
+}
+
+// Convergence check of the stopped base (section 2.1 runs the base until
+// convergence or for a fixed number of steps).  After step t the plan
+// P^(t,t) = exp(S + u^(t) (+) v^(t)) has exact column sums b, and its row sums
+// are a_i 2^(u^(t)_i - u^(t+1)_i) (log2 units) with u^(t+1) = U(v^(t)), the
+// row update of the next step.  So
+//   e_t = sum_i |rowsum_i(P^(t,t)) - a_i| = sum_i a_i |2^(u^(t)_i - u^(t+1)_i) - 1|
+// over the active rows (the dustbin row included), in fp64 and a fixed order.
+// The step carrying the check left u^(t+1) in `unew` and the latest-u buffer
+// untouched; this kernel also moves the potentials on: u^(t) to `uold_copy`
+// (the stopped-base slot, should the check pass) and u^(t+1) to the latest-u
+// buffer.  One workgroup per (b, h).
+__global__ __launch_bounds__(256) void base_check(Geom g, const float* a, double* ubuf, const double* unew,
+                                                  double* uold_copy, double* err) {
+  const int bh = blockIdx.x;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const size_t L = g.L;
+  const int tid = threadIdx.x;
+  const int last = g.dustbin ? n : n - 1;  // last active index
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = tid; i <= last; i += 256) {
+    const size_t o = (size_t)bh * L + i;
+    const double uo = ubuf[o], un = unew[o];
+    acc += (double)a[(size_t)bb * L + i] * fabs(expm1((uo - un) * 0.6931471805599453));
+    uold_copy[o] = uo;
+    ubuf[o] = un;
+  }
+  red[tid] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) err[bh] = red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -1299,13 +1341,18 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     hipLaunchKernelGGL(dustbin_scores<T>, sg, dim3(256), 0, st, g, reinterpret_cast<const T*>(f.Q),
                        reinterpret_cast<const T*>(f.K), w.sdr, w.sdc);
   }
-  const int N = f.T + f.R;
   if (f.T == 0) {
     dim3 zg((g.L + 255) / 256, nbh);
     hipLaunchKernelGGL(zero_start, zg, dim3(256), 0, st, g, w.tail_u, w.tail_v);
   }
   const size_t part_slot = (size_t)nbh * g.nseg * g.SW;
-  for (int t = 1; t <= N; ++t) {
+  const bool stop_early = f.stop.every > 0;
+  // Step t of a run whose base has T steps.  A checked step (t = c + 1 after
+  // a check point c) writes u^(t) only to tail slot 1 and v^(t-1) to slot 0,
+  // so that it is the first tail step if the check passes; base_check then
+  // moves the latest-u buffer on.
+  auto launch_step = [&](int t, int Tbase, bool check) {
+    const int N = Tbase + f.R;
     IterArgs a{};
     a.Q = f.Q;
     a.K = f.K;
@@ -1315,9 +1362,14 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     a.part_in = (t == 1) ? nullptr : w.part + (size_t)((t - 1) & 1) * part_slot;
     a.v_prev2 = (t <= 2) ? nullptr : w.vbuf + (size_t)((t - 2) & 1) * BHL;
     a.v_out = (t == 1) ? nullptr : w.vbuf + (size_t)((t - 1) & 1) * BHL;
-    a.v_tail = (t >= 2 && t - 1 >= f.T) ? w.tail_v + (size_t)(t - 1 - f.T) * BHL : nullptr;
+    a.v_tail = (t >= 2 && t - 1 >= Tbase) ? w.tail_v + (size_t)(t - 1 - Tbase) * BHL : nullptr;
     a.u_out = w.ubuf;
-    a.u_tail = (t >= f.T) ? w.tail_u + (size_t)(t - f.T) * BHL : nullptr;
+    a.u_tail = (t >= Tbase) ? w.tail_u + (size_t)(t - Tbase) * BHL : nullptr;
+    if (check) {
+      a.v_tail = w.tail_v;
+      a.u_out = w.tail_u + BHL;
+      a.u_tail = nullptr;
+    }
     a.part_out = w.part + (size_t)(t & 1) * part_slot;
     a.partd_out = w.partd + (size_t)(t & 1) * nbh * g.nseg;
     a.dstate = (g.dustbin && t > 1) ? w.dstate : nullptr;
@@ -1325,8 +1377,10 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     a.sdc = w.sdc;
     a.padded_grid = iter_grid;
     // timing brackets: the whole run of step launches, or each launch when
-    // the dustbin kernel runs between them
-    if (timing_enabled() && (g.dustbin || t == 1)) timing_mark(st, false);
+    // the dustbin kernel runs between them (not kept when the base may stop
+    // early: the host waits at every check)
+    const bool tm = timing_enabled() && !stop_early;
+    if (tm && (g.dustbin || t == 1)) timing_mark(st, false);
     if (g.NT <= 3)
       hipLaunchKernelGGL((iter_kernel<T, D, 3>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
     else if (g.NT <= 5)
@@ -1335,7 +1389,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       hipLaunchKernelGGL((iter_kernel<T, D, 9>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
     else
       hipLaunchKernelGGL((iter_kernel<T, D, kMaxTiles>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
-    if (timing_enabled() && (g.dustbin || t == N)) timing_mark(st, true, g.dustbin ? 1 : N);
+    if (tm && (g.dustbin || t == N)) timing_mark(st, true, g.dustbin ? 1 : N);
     if (g.dustbin) {
       DustArgs da{};
       da.a = f.a;
@@ -1345,12 +1399,53 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       da.dstate = w.dstate;
       da.sdr = w.sdr;
       da.u_tail = a.u_tail;
-      da.v_tail = (t >= f.T) ? w.tail_v + (size_t)(t - f.T) * BHL : nullptr;
-      da.u_out = w.ubuf;
+      da.v_tail = (t >= Tbase) ? w.tail_v + (size_t)(t - Tbase) * BHL : nullptr;
+      da.u_out = a.u_out;
+      if (check) {
+        da.v_tail = w.tail_v + BHL;
+        da.v_prev_tail = w.tail_v;
+      }
       da.first = (t == 1);
       hipLaunchKernelGGL(dustbin_step, dim3(nbh), dim3(256), 0, st, g, da);
     }
+  };
+  // Base: T steps, or (early stop) up to T steps with a check of e_c (see
+  // base_check) carried by step c + 1 for c = every, 2 every, ... while
+  // c + 2 <= T.  The base ends at the first c with max over (b, h) of
+  // e_c < tol; step c + 1 is then the first tail step.
+  int Tb = f.T;
+  int t = 1;
+  if (stop_early) {
+    std::vector<double> eh((size_t)nbh);
+    for (; t <= f.T; ++t) {
+      const int c = t - 1;
+      const bool check = c >= 1 && c % f.stop.every == 0 && c + 2 <= f.T;
+      launch_step(t, f.T, check);
+      if (!check) continue;
+      hipLaunchKernelGGL(base_check, dim3(nbh), dim3(256), 0, st, g, f.a, w.ubuf, w.tail_u + BHL, w.tail_u,
+                         w.err);
+      err = hipMemcpyAsync(eh.data(), w.err, (size_t)nbh * sizeof(double), hipMemcpyDeviceToHost, st);
+      if (err == hipSuccess) err = hipStreamSynchronize(st);
+      if (err != hipSuccess) return err;
+      double emax = 0.0;
+      bool finite = true;
+      for (double e : eh) {
+        finite = finite && e == e;
+        emax = e > emax ? e : emax;
+      }
+      if (f.stop.err_last) *f.stop.err_last = finite ? emax : NAN;
+      if (finite && emax < f.stop.tol) {
+        Tb = c;
+        ++t;
+        break;
+      }
+    }
+  } else {
+    for (; t <= f.T; ++t) launch_step(t, f.T, false);
   }
+  for (; t <= Tb + f.R; ++t) launch_step(t, Tb, false);
+  if (f.stop.T_used) *f.stop.T_used = Tb;
+  const int N = Tb + f.R;
   OutArgs o{};
   o.Q = f.Q;
   o.K = f.K;

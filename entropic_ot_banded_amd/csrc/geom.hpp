@@ -61,6 +61,7 @@ struct Workspace {
   float* sdr;      // [BHL] dustbin row scores (log2 units)
   float* sdc;      // [BHL] dustbin column scores (log2 units)
   float* bw;       // backward vectors [(3R + 8) * BHL]
+  double* err;     // [BH] base convergence check (row-marginal L1 error)
   size_t floats;
 };
 
@@ -83,6 +84,7 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.sdr = take(BHL);
   w.sdc = take(BHL);
   w.bw = take((size_t)(3 * R + 8) * BHL);
+  w.err = take_d(BH);
   w.floats = off;
   return w;
 }
@@ -94,6 +96,15 @@ inline Workspace carve(float* base, const Geom& g, int R) {
 bool timing_enabled();
 void timing_mark(hipStream_t st, bool end, int launches = 1);
 
+// Early stop of the stopped base (see sinkattn_forward_converge): check
+// every `every` steps (0 = fixed T); the base length used goes to *T_used.
+struct BaseStop {
+  int every;
+  double tol;
+  int* T_used;       // host pointer
+  double* err_last;  // host pointer, optional: largest per-(b, h) error at the last check
+};
+
 // Arguments of the host launchers (device pointers).
 struct FwdLaunch {
   const void* Q;
@@ -104,7 +115,8 @@ struct FwdLaunch {
   float* O;
   float* u;
   float* v;
-  int T, R;
+  int T, R;      // T: base steps (the maximum when stop.every > 0)
+  BaseStop stop; // zero-initialised: fixed T
 };
 
 struct BwdLaunch {

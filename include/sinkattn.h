@@ -119,6 +119,37 @@ int sinkattn_forward(const void *Q, const void *K, const void *V, int W, int T, 
                      float *O, float *u, float *v, void *workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
+/* Forward pass whose stopped base ends early once converged (section 2.1:
+ * the base runs until convergence or for a fixed number of steps).
+ * Arguments as sinkattn_forward, with T_max (>= 0) the largest base length
+ * and R >= 1.  The convergence measure after base step c is the L1 row-
+ * marginal error of its plan,
+ *   e_c = sum over active rows i of | sum_j P^(c,c)_ij - a_i |,
+ * P^(c,c) = exp(S + u^(c) (+) v^(c)) on the support (its column sums are b
+ * exactly), per (b, h) problem, evaluated in fp64 from the potentials.  It is
+ * checked for c = check_every, 2 check_every, ... while c + 2 <= T_max; the
+ * base ends at the first checked c where every (b, h) has e_c < tol (so all
+ * problems of a call share one base length), otherwise after T_max steps.
+ * The check of c rides on the row update of step c + 1, which is then the
+ * first tail step, so a passing check costs no extra step.
+ *   tol         : >= 0 (0 never stops early).  Values below about 1e-6 sit
+ *                 under the resolution of fp32 entry sums.
+ *   check_every : >= 1.
+ *   T_used      : out (host int): the base length used (the T to pass to
+ *                 sinkattn_backward; any T is accepted there).
+ *   err_last    : out (host double, may be NULL): the largest per-(b, h)
+ *                 e_c at the last check (NaN if a check was not finite;
+ *                 untouched if no check ran).
+ * Blocks the calling thread at each check (a device-to-host copy of B*H
+ * doubles and a stream synchronisation).  Argument errors return before
+ * anything is enqueued; a HIP error found at a check returns SINKATTN_EHIP
+ * after the launches before it. */
+int sinkattn_forward_converge(const void *Q, const void *K, const void *V, int W, int T_max,
+                              int R, const float *a, const float *b, const sinkattn_shape *s,
+                              double tol, int check_every, float *O, float *u, float *v,
+                              void *workspace, size_t workspace_bytes, int *T_used,
+                              double *err_last, hipStream_t stream);
+
 /* Backward pass: exact adjoint of the R tail steps with the stopped base held
  * constant (section 2.2), evaluated with the single-reference-tile schedule.
  *   Q, K, V, W, T, R, a, b, s : exactly as passed to sinkattn_forward.

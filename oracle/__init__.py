@@ -18,3 +18,6 @@ from .sinkhorn import (  # noqa: F401
 )
 from .sinkhorn import _Problem as Problem  # noqa: F401
 from .sinkhorn import backward_one, bptt_one, forward_one  # noqa: F401
+from .sinkhorn import (  # noqa: F401
+    base_errors, converged_base_length, row_marginal_error, select_base_length,
+)

@@ -23,6 +23,10 @@ design notes):
 * Stopped base (section 2.1): T steps treated as constants -> (u0, v0).
 * Differentiable tail (section 2.1): R further steps u^(r) = U(v^(r-1)),
   v^(r) = V(u^(r)), r = 1..R.
+* Convergence-controlled base (section 2.1 allows running the base until
+  convergence): the L1 row-marginal error of the plan after base step c,
+  sum_i |sum_j P^(c,c)_ij - a_i|, checked every k steps; a batch stops at the
+  first check where every problem is below the tolerance.
 * Output: P = exp(S + u^(R) (+) v^(R)) on Omega, O = P V.
 * Exact tail adjoint (section 2.2): reverse-mode through the R tail steps
   with the base held constant.  Every staircase plan P^(r,s) =
@@ -50,6 +54,7 @@ __all__ = [
     "band_offsets", "Support", "scores", "row_update", "col_update",
     "solve", "Solution", "output", "adjoint", "Grads",
     "forward_batch", "backward_batch", "bptt_batch", "forward_backward_batch",
+    "row_marginal_error", "base_errors", "select_base_length", "converged_base_length",
 ]
 
 
@@ -295,6 +300,63 @@ def forward_one(q, k, vv, a, b, sup: Support, T: int, R: int,
     us = [_inactive_to_neg_inf(x, act) for x in us]
     vs = [_inactive_to_neg_inf(x, act) for x in vs]
     return Solution(us, vs, O)
+
+
+# ---------------------------------------------------------------------------
+# Convergence-controlled stopped base (section 2.1: the base is run until
+# convergence or for a fixed number of steps)
+# ---------------------------------------------------------------------------
+
+def row_marginal_error(pb: _Problem, u: np.ndarray, v: np.ndarray) -> float:
+    """L1 row-marginal error of the plan P = exp(S + u (+) v), built
+    explicitly: sum over active rows i of |sum_j P_ij - a_i|."""
+    act = pb.sup.active
+    rs = pb.row_sums(pb.plan(u, v))
+    return float(np.sum(np.abs(rs[act] - pb.a[act])))
+
+
+def base_errors(pb: _Problem, T_max: int, every: int) -> dict:
+    """Run the base from u = v = 0 for T_max steps and record, for every
+    checked step c (c a multiple of `every` with c + 2 <= T_max), the error
+    of the plan after step c: {c: row_marginal_error(u^(c), v^(c))}."""
+    L = pb.sup.L
+    u = np.zeros(L)
+    v = np.zeros(L)
+    errs = {}
+    for c in range(1, T_max + 1):
+        u = pb.U(v)
+        v = pb.V(u)
+        if c % every == 0 and c + 2 <= T_max:
+            errs[c] = row_marginal_error(pb, u, v)
+    return errs
+
+
+def select_base_length(errs: Sequence[dict], T_max: int, tol: float) -> int:
+    """Base length for a batch of problems: the first checked step at which
+    every problem's error is below tol, else T_max."""
+    checks = sorted(set().union(*[set(e) for e in errs])) if errs else []
+    for c in checks:
+        if all(c in e and e[c] < tol for e in errs):
+            return c
+    return T_max
+
+
+def _job_base_errors(args):
+    q, k, a, b, L, n, W, dustbin, T_max, every = args
+    pb = _Problem(q, k, a, b, Support.build(L, n, W, dustbin))
+    return base_errors(pb, T_max, every)
+
+
+def converged_base_length(Q, K, a, b, W, T_max, tol, every, lengths=None, dustbin=False,
+                          processes: Optional[int] = None):
+    """(T_used, per-problem error dicts) of the convergence-controlled base
+    over a [B, H, L, d] batch; the forward then runs with T = T_used."""
+    B, H, L, d = Q.shape
+    ns = _lengths_of(L, lengths, B)
+    jobs = [(Q[bi, h], K[bi, h], a[bi], b[bi], L, ns[bi], W, dustbin, T_max, every)
+            for bi in range(B) for h in range(H)]
+    errs = _map(_job_base_errors, jobs, processes)
+    return select_base_length(errs, T_max, tol), errs
 
 
 # ---------------------------------------------------------------------------

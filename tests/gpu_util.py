@@ -94,6 +94,38 @@ def run_gpu(prob: workloads.Problem, T=None, R=None, W=None, want_vbar0=False, b
     return res
 
 
+def run_gpu_converge(prob: workloads.Problem, T_max, tol, every, R=None, W=None, backward=True):
+    """forward_converge (+ backward at the base length it used).  Returns the
+    same dict as run_gpu plus T_used and err_last."""
+    import torch
+
+    import entropic_ot_banded_amd as eoba
+
+    R = prob.R if R is None else R
+    W = prob.W if W is None else W
+    t = to_device(prob)
+    O, u, v, ws, T_used, err_last = eoba.forward_converge(
+        t["Q"], t["K"], t["V"], W, T_max, R, t["a"], t["b"], tol, every, t["lengths"], prob.dustbin)
+    out = {"O": O, "u": u, "v": v}
+    us, vs = eoba.tail_stack(ws, t["Q"], R, t["lengths"], prob.dustbin)
+    out["us"] = [x.clone() for x in us]
+    out["vs"] = [x.clone() for x in vs]
+    if backward:
+        dQ, dK, dV, _ = eoba.backward(t["Q"], t["K"], t["V"], W, T_used, R, t["a"], t["b"], O, t["dO"],
+                                      ws, t["lengths"], prob.dustbin)
+        out.update(dQ=dQ, dK=dK, dV=dV)
+    torch.cuda.synchronize()
+    res = {}
+    for k, val in out.items():
+        if isinstance(val, list):
+            res[k] = np.stack([x.cpu().numpy() for x in val])
+        else:
+            res[k] = val.float().cpu().numpy()
+    res["T_used"] = T_used
+    res["err_last"] = err_last
+    return res
+
+
 def run_oracle(prob: workloads.Problem, T=None, R=None, W=None, backward=True, processes=None):
     T = prob.T if T is None else T
     R = prob.R if R is None else R

@@ -111,6 +111,28 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, sh, ws_bytes=1024) == binding.SINKATTN_EWORKSPACE
 
 
+def test_forward_converge_validation_before_launch(lib):
+    sh = _shape()
+    s = sh.c()
+    fake = ctypes.c_void_p(0x10000)
+    nb = eoba.workspace_bytes(sh, 64, 2)
+    t_used = ctypes.c_int32(-7)
+
+    def call(T_max=10, R=2, tol=1e-3, every=2, ws=nb, tu=True):
+        return lib.sinkattn_forward_converge(
+            fake, fake, fake, 64, T_max, R, fake, fake, ctypes.byref(s), tol, every, fake, fake,
+            fake, fake, ws, ctypes.byref(t_used) if tu else None, None, ctypes.c_void_p(None))
+
+    assert call(R=0) == binding.SINKATTN_EINVAL       # the check rides on a tail step
+    assert call(every=0) == binding.SINKATTN_EINVAL
+    assert call(tol=-1.0) == binding.SINKATTN_EINVAL
+    assert call(tol=float("nan")) == binding.SINKATTN_EINVAL
+    assert call(T_max=-1) == binding.SINKATTN_EINVAL
+    assert call(tu=False) == binding.SINKATTN_EINVAL
+    assert call(ws=1024) == binding.SINKATTN_EWORKSPACE
+    assert t_used.value == -7  # nothing written on a rejected call
+
+
 def test_backward_validation_before_launch(lib):
     sh = _shape()
     s = sh.c()

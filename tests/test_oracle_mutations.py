@@ -21,8 +21,8 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "sinkhorn.py")
 
 MUTANTS = {
-    "column update first": ("        u = pb.U(v)\n        v = pb.V(u)\n",
-                            "        v = pb.V(u)\n        u = pb.U(v)\n"),
+    "column update first": ("    for _ in range(T):\n        u = pb.U(v)\n        v = pb.V(u)\n",
+                            "    for _ in range(T):\n        v = pb.V(u)\n        u = pb.U(v)\n"),
     "symmetric band": ("return W // 2, (W + 1) // 2 - 1", "return W // 2, W // 2"),
     "no dustbin corner": ("rows.append(np.full(n + 1, dlt, dtype=np.int64))\n"
                           "            cols.append(np.arange(n + 1, dtype=np.int64))",
@@ -42,6 +42,12 @@ MUTANTS = {
     "E term dropped": ("vbar = pb.col_sums(P * dP)", "vbar = np.zeros(sup.L)"),
     "output uses previous v": ("O = output(pb, us[-1], vs[-1], vv)",
                                "O = output(pb, us[-1], vs[-2] if len(vs) > 1 else vs[-1], vv)"),
+    "base check against b": ("return float(np.sum(np.abs(rs[act] - pb.a[act])))",
+                             "return float(np.sum(np.abs(rs[act] - pb.b[act])))"),
+    "base check on column sums": ("rs = pb.row_sums(pb.plan(u, v))",
+                                  "rs = pb.col_sums(pb.plan(u, v))"),
+    "base check before the column update": ("        v = pb.V(u)\n        if c % every == 0",
+                                            "        if c % every == 0"),
 }
 
 
@@ -103,6 +109,21 @@ def _checks(m):
         mask = refs.support_mask(L, n, W, dust)
         tq, tk, tv, _ = refs.torch_surrogate_grads(q, k, vv, a, b, mask, T, R, dO)
         yield f"grad{(L, n, dust)}", max(_rel(g.dQ, tq), _rel(g.dK, tk), _rel(g.dV, tv)) < 1e-10
+    # convergence-controlled base: errors of the dense textbook plan
+    L, n, W = 14, 11, 5
+    p = workloads.custom(B=1, H=1, L=L, d=4, W=W, T=9, R=1, lengths=[n], seed=9, scale=1.4)
+    q, k, vv = p.Q[0, 0], p.K[0, 0], p.V[0, 0]
+    a, b = _random_marginals(p, 3)
+    mask = refs.support_mask(L, n, W)
+    X = np.where(mask, q.astype(np.float64) @ k.astype(np.float64).T / math.sqrt(4), -np.inf)
+    pb = m._Problem(q, k, a, b, m.Support.build(L, n, W))
+    got = m.base_errors(pb, 9, 2)
+    ok = sorted(got) == [2, 4, 6]
+    for c in (2, 4, 6):
+        us, vs, _ = refs.dense_sinkhorn(q, k, vv, a, b, mask, c, 0)
+        want = np.abs(refs.plan_dense(X, us[0], vs[0]).sum(axis=1)[:n] - a[:n]).sum()
+        ok = ok and c in got and abs(got[c] - want) <= 1e-12 * max(1.0, want)
+    yield "base check", ok
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -367,3 +367,84 @@ def test_gradient_gap_shrinks_with_tail_depth(cfg):
         gaps[R] = np.linalg.norm(gv - refv) / np.linalg.norm(refv)
     assert gaps[0] > gaps[1] > gaps[2], gaps
     assert gaps[4] <= gaps[2] * 1.0001, gaps
+
+
+# --- convergence-controlled base (section 2.1: "until convergence") ------------
+
+def _dense_errors(q, k, vv, a, b, mask, T_max, every):
+    """Row-marginal L1 errors of the plan after each checked step, from the
+    textbook dense Sinkhorn of refs (an independent implementation)."""
+    out = {}
+    for c in range(every, T_max - 1, every):
+        us, vs, _ = refs.dense_sinkhorn(q, k, vv, a, b, mask, c, 0)
+        X = np.where(mask, np.asarray(q, np.float64) @ np.asarray(k, np.float64).T /
+                     math.sqrt(q.shape[1]), -np.inf)
+        P = refs.plan_dense(X, us[0], vs[0])
+        act = mask.any(axis=1)
+        out[c] = float(np.abs(P.sum(axis=1)[act] - np.asarray(a, np.float64)[act]).sum())
+    return out
+
+
+@pytest.mark.parametrize("L,n,W,dust", [(24, 24, 7, False), (24, 17, 6, True)])
+def test_base_errors_match_dense_plan(L, n, W, dust):
+    """e_c from the oracle equals the L1 row error of the dense textbook plan."""
+    p = workloads.custom(B=1, H=1, L=L, d=4, W=W, T=12, R=1, lengths=None if n == L else [n],
+                         dustbin=dust, seed=3, scale=1.5)
+    q, k, vv = p.Q[0, 0], p.K[0, 0], p.V[0, 0]
+    rng = np.random.default_rng(7)
+    act = refs.support_mask(L, n, W, dust).any(axis=1)
+    a = np.where(act, rng.random(L) + 0.3, 0.0)
+    b = np.where(act, rng.random(L) + 0.3, 0.0)
+    a, b = a / a.sum(), b / b.sum()
+    pb = oracle.sinkhorn._Problem(q, k, a, b, oracle.Support.build(L, n, W, dust))
+    got = oracle.base_errors(pb, 12, 3)
+    want = _dense_errors(q, k, vv, a, b, refs.support_mask(L, n, W, dust), 12, 3)
+    assert sorted(got) == sorted(want) == [3, 6, 9]
+    for c in want:
+        assert abs(got[c] - want[c]) <= 1e-12 * max(1.0, want[c]), (c, got[c], want[c])
+        assert want[c] > 1e-8  # a non-trivial check: not yet converged
+
+
+def test_base_error_closed_form_from_next_row_update():
+    """After a full step the column sums are b, and the row sums of P^(c,c)
+    are a_i exp(u^(c)_i - u^(c+1)_i) with u^(c+1) = U(v^(c))."""
+    p = workloads.make(2)
+    q, k, vv, a, b = _one(p)
+    rng = np.random.default_rng(1)
+    a = rng.random(p.L) + 0.5
+    a = a / a.sum()
+    pb = oracle.sinkhorn._Problem(q, k, a, b, oracle.Support.build(p.L, p.L, p.W))
+    u = np.zeros(p.L)
+    v = np.zeros(p.L)
+    for c in range(1, 7):
+        u = pb.U(v)
+        v = pb.V(u)
+        e = oracle.row_marginal_error(pb, u, v)
+        closed = float(np.sum(a * np.abs(np.expm1(u - pb.U(v)))))
+        assert abs(e - closed) <= 1e-12 * max(e, 1e-300), (c, e, closed)
+        colerr = np.abs(pb.col_sums(pb.plan(u, v)) - pb.b).sum()
+        assert colerr < 1e-14
+
+
+def test_zero_scores_converge_in_one_step():
+    """S = 0 on a dense support with uniform marginals: one step solves the
+    problem (P = a b^T), so e_c = 0 and the base stops at the first check."""
+    L = 16
+    q = np.zeros((L, 4))
+    a = np.full(L, 1.0 / L)
+    pb = oracle.sinkhorn._Problem(q, q, a, a, oracle.Support.build(L, L, 2 * L - 1))
+    errs = oracle.base_errors(pb, 10, 2)
+    assert all(e < 1e-15 for e in errs.values())
+    assert oracle.select_base_length([errs], 10, 1e-12) == 2
+
+
+def test_select_base_length_rule():
+    """The batch stops at the first check where every problem is below tol."""
+    e1 = {2: 1e-2, 4: 1e-4, 6: 1e-7}
+    e2 = {2: 1e-3, 4: 1e-3, 6: 1e-8}
+    assert oracle.select_base_length([e1, e2], 9, 1e-2) == 4
+    assert oracle.select_base_length([e1, e2], 9, 5e-3) == 4
+    assert oracle.select_base_length([e1, e2], 9, 5e-4) == 6
+    assert oracle.select_base_length([e1, e2], 9, 1e-9) == 9
+    assert oracle.select_base_length([e1, {2: float("nan"), 4: 0.0, 6: 0.0}], 9, 1.0) == 4
+    assert oracle.select_base_length([{}], 3, 1.0) == 3
