@@ -259,6 +259,9 @@ def main():
     ap.add_argument("--converge-tol", type=float, default=5e-5,
                     help="also time the early-stopping base at this tolerance (0: skip)")
     ap.add_argument("--converge-every", type=int, default=5)
+    ap.add_argument("--certificate-rmax", type=int, default=4,
+                    help="also time the stop-gradient bias certificate up to this depth (0: skip)")
+    ap.add_argument("--certificate-tau", type=float, default=1e-5)
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
@@ -352,6 +355,24 @@ def main():
                      "tokens_per_s": round(prob.real_tokens() / (c_ms * 1e-3), 1),
                      "timing": "host clock, median of 5 forward_converge + backward"}
 
+    # Stop-gradient bias certificate: a forward keeping R_max tail steps, then
+    # eta_R for R = 0..R_max (R_max + 1 backward passes) and the selected depth.
+    certificate = None
+    if args.certificate_rmax > 0:
+        Rm = args.certificate_rmax
+        Oc, _, _, wsc = eoba.forward(Q, K, V, W, T, Rm, a, b)
+        eoba.tail_certificate(Q, K, V, W, T, Rm, a, b, Oc, dO, wsc)  # warm
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        _, _, _, eta = eoba.tail_certificate(Q, K, V, W, T, Rm, a, b, Oc, dO, wsc)
+        torch.cuda.synchronize()
+        c_ms = (time.perf_counter() - c0) * 1e3
+        certificate = {"T": T, "R_max": Rm, "eta": [float(f"{x:.4e}") for x in eta],
+                       "tau": args.certificate_tau,
+                       "selected_R": eoba.select_tail_depth(eta, args.certificate_tau),
+                       "ms": round(c_ms, 3), "timing": "host clock, one call (R_max + 1 backward passes)"}
+        del Oc, wsc
+
     if args.copy_calibration:
         x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         y = torch.empty_like(x)
@@ -399,6 +420,8 @@ def main():
            "roofline": roofline, "path_roofline": path}
     if converged is not None:
         out["converged_base"] = converged
+    if certificate is not None:
+        out["certificate"] = certificate
     if not args.no_cpu_baseline:
         cb = cpu_baseline(prob, args.cpu_heads)
         cb.pop("seconds", None)

@@ -25,7 +25,7 @@ SINKATTN_F32 = 0
 SINKATTN_BF16 = 1
 
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
-            "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_timing_enable", "sinkattn_timing_collect",
+            "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate", "sinkattn_timing_enable", "sinkattn_timing_collect",
             "sinkattn_status_string", "sinkattn_version")
 
 
@@ -69,6 +69,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_backward.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, sz,
                                       vp, vp, vp, vp, vp]
     lib.sinkattn_backward.restype = i32
+    lib.sinkattn_tail_certificate.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, sz,
+                                              vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.sinkattn_tail_certificate.restype = i32
     lib.sinkattn_timing_enable.argtypes = [i32]
     lib.sinkattn_timing_enable.restype = i32
     lib.sinkattn_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -263,6 +266,38 @@ def backward(Q, K, V, W: int, T: int, R: int, a, b, O, dO, workspace, lengths=No
         _stream(Q.device))
     _check(st)
     return dQ, dK, dV, vbar0
+
+
+def tail_certificate(Q, K, V, W: int, T: int, R_max: int, a, b, O, dO, workspace, lengths=None,
+                     dustbin: bool = False):
+    """Stop-gradient bias certificate of a forward run with tail depth R_max.
+    Returns (dQ, dK, dV, eta): the gradients at depth R_max and
+    eta[R] = ||grad_Rmax - grad_R|| / ||grad_Rmax|| over (dQ, dK) for
+    R = 0..R_max (see sinkattn_tail_certificate).  Blocks until done."""
+    torch = _torch()
+    _validate(Q, K, V, a, b, lengths)
+    if dO.shape != Q.shape or dO.dtype != Q.dtype or not dO.is_contiguous():
+        raise ValueError("dO must match Q in shape and dtype and be contiguous")
+    shape = _shape_of(Q, lengths, dustbin)
+    mk = lambda: torch.empty(Q.shape, dtype=torch.float32, device=Q.device)  # noqa: E731
+    dQ, dK, dV, sQ, sK = mk(), mk(), mk(), mk(), mk()
+    eta = (ctypes.c_double * (R_max + 1))()
+    s = shape.c()
+    st = load_library().sinkattn_tail_certificate(
+        _ptr(Q), _ptr(K), _ptr(V), W, T, R_max, _ptr(a), _ptr(b), ctypes.byref(s), _ptr(O), _ptr(dO),
+        _ptr(workspace), workspace.numel(), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(sQ), _ptr(sK), eta,
+        _stream(Q.device))
+    _check(st)
+    return dQ, dK, dV, [float(x) for x in eta]
+
+
+def select_tail_depth(eta, tau: float) -> int:
+    """Smallest tail depth R whose certificate eta[R] is below tau (the
+    deepest, len(eta) - 1, when none is)."""
+    for R, e in enumerate(eta):
+        if e < tau:
+            return R
+    return len(eta) - 1
 
 
 def tail_stack(workspace, Q, R: int, lengths=None, dustbin=False):

@@ -16,6 +16,8 @@ namespace sinkattn {
 
 hipError_t launch_forward(const Geom& g, int dtype, const FwdLaunch& f, const Workspace& w, hipStream_t st);
 hipError_t launch_backward(const Geom& g, int dtype, const BwdLaunch& f, const Workspace& w, hipStream_t st);
+hipError_t launch_certificate(const Geom& g, int dtype, const BwdLaunch& base, int R_max, const Workspace& w,
+                              float* dQs, float* dKs, double* eta, hipStream_t st);
 
 namespace {
 
@@ -258,6 +260,29 @@ int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T,
   if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
   BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, vbar0, T, R};
   hipError_t e = launch_backward(g, s->dtype, f, w, stream);
+  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
+  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+}
+
+int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W, int T, int R_max, const float* a,
+                              const float* b, const sinkattn_shape* s, const float* O, const void* dO,
+                              void* workspace, size_t workspace_bytes, float* dQ, float* dK, float* dV,
+                              float* dQ_scratch, float* dK_scratch, double* eta, hipStream_t stream) {
+  if (!Q || !K || !V || !a || !b || !O || !dO || !workspace || !dQ || !dK || !dV || !dQ_scratch ||
+      !dK_scratch || !eta)
+    return SINKATTN_EINVAL;
+  if (T < 0 || R_max < 1) return SINKATTN_EINVAL;
+  if (R_max > kMaxTailBackward || R_max > kMaxCertR) return SINKATTN_EUNSUPPORTED;
+  Geom g;
+  int st = make_geom(s, W, &g);
+  if (st != SINKATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) ||
+      !aligned16(dV) || !aligned16(dQ_scratch) || !aligned16(dK_scratch) || !aligned16(workspace))
+    return SINKATTN_EINVAL;
+  Workspace w = carve(static_cast<float*>(workspace), g, R_max);
+  if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
+  BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, nullptr, T, R_max};
+  hipError_t e = launch_certificate(g, s->dtype, f, R_max, w, dQ_scratch, dK_scratch, eta, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
   return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
 }

@@ -1136,8 +1136,11 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   p.O = f.O;
   p.a = f.a;
   p.b = f.b;
-  p.tail_u = w.tail_u;
-  p.tail_v = w.tail_v;
+  // this pass's stack: slots slot0 .. slot0 + R of the forward's tail stack
+  const double* tail_u = w.tail_u + (size_t)f.slot0 * BHL;
+  const double* tail_v = w.tail_v + (size_t)f.slot0 * BHL;
+  p.tail_u = tail_u;
+  p.tail_v = tail_v;
   p.sdr = w.sdr;
   p.sdc = w.sdc;
   p.D = Dv;
@@ -1182,7 +1185,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
   else
     hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
-  hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, w.tail_u, w.tail_v, w.sdr, R, f.dV,
+  hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, tail_u, tail_v, w.sdr, R, f.dV,
                      vbar + (size_t)R * BHL);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
   // adjoint vectors through the tail

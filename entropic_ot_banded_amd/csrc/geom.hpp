@@ -62,10 +62,14 @@ struct Workspace {
   float* sdc;      // [BHL] dustbin column scores (log2 units)
   float* bw;       // backward vectors [(3R + 8) * BHL]
   double* err;     // [BH] base convergence check (row-marginal L1 error)
+  double* red;     // [kRedParts][2] + [kMaxCertR + 1][4] norm reductions of the tail certificate
   size_t floats;
 };
 
 inline size_t align64(size_t n) { return (n + 63) & ~size_t(63); }
+
+constexpr int kRedParts = 1024;  // workgroups of the certificate's norm reduction
+constexpr int kMaxCertR = 8;     // deepest tail the certificate compares against
 
 inline Workspace carve(float* base, const Geom& g, int R) {
   const size_t BHL = (size_t)g.B * g.H * g.L;
@@ -85,6 +89,7 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.sdc = take(BHL);
   w.bw = take((size_t)(3 * R + 8) * BHL);
   w.err = take_d(BH);
+  w.red = take_d(2 * kRedParts + 4 * (kMaxCertR + 1));
   w.floats = off;
   return w;
 }
@@ -132,6 +137,8 @@ struct BwdLaunch {
   float* dV;
   float* vbar0;
   int T, R;
+  int slot0;  // tail-stack slot of this pass's u^(0), v^(0): R_fwd - R when the
+              // forward kept a deeper tail R_fwd (0 otherwise)
 };
 
 }  // namespace sinkattn

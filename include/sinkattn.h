@@ -167,6 +167,32 @@ int sinkattn_backward(const void *Q, const void *K, const void *V, int W, int T,
                       size_t workspace_bytes, float *dQ, float *dK, float *dV,
                       float *vbar0, hipStream_t stream);
 
+/* A-posteriori certificate of the stop-gradient bias, for choosing the tail
+ * depth (section 2.4, third certificate; section 4.1).  The forward must have
+ * run with tail depth R_max (the same W, T, shape; workspace carved for
+ * R_max), i.e. N = T + R_max steps.  For R in [0, R_max], grad_R is the exact
+ * gradient of that N-step forward with only its last R steps differentiable
+ * (what sinkattn_backward returns for a forward with T' = N - R, R).
+ *   eta[R] = ||grad_Rmax - grad_R||_F / ||grad_Rmax||_F over (dQ, dK) of the
+ *            whole call (dV does not depend on R), fp64; eta[R_max] = 0.
+ * With T = 0, grad_Rmax is the full gradient through every step and eta[R]
+ * is the exact residual of stopping the gradient after R steps; otherwise it
+ * is the residual against the deepest tail computed.  The smallest R with
+ * eta[R] < tau is the depth the certificate selects for tolerance tau.
+ *   dQ, dK, dV  : out, fp32 [B, H, L, d]: grad_Rmax (as sinkattn_backward).
+ *   dQ_scratch, dK_scratch : device fp32 [B, H, L, d] scratch.
+ *   eta         : out, host double[R_max + 1].
+ *   R_max       : 1 .. 8.
+ * Runs R_max + 1 backward passes and blocks the calling thread until the
+ * stream has finished them.  Argument errors return before anything is
+ * enqueued. */
+int sinkattn_tail_certificate(const void *Q, const void *K, const void *V, int W, int T,
+                              int R_max, const float *a, const float *b,
+                              const sinkattn_shape *s, const float *O, const void *dO,
+                              void *workspace, size_t workspace_bytes, float *dQ, float *dK,
+                              float *dV, float *dQ_scratch, float *dK_scratch, double *eta,
+                              hipStream_t stream);
+
 /* Diagnostics for benchmarking: timing of the fused Sinkhorn step kernel,
  * which dominates the run time.  While enabled (on != 0), sinkattn_forward
  * records HIP events on the caller's stream around its step-kernel launches:

@@ -28,6 +28,10 @@ design notes):
   sum_i |sum_j P^(c,c)_ij - a_i|, checked every k steps; a batch stops at the
   first check where every problem is below the tolerance.
 * Output: P = exp(S + u^(R) (+) v^(R)) on Omega, O = P V.
+* Bias certificate (section 2.4, third certificate): for one forward of
+  N = T + R_max steps, eta_R = ||g_Rmax - g_R|| / ||g_Rmax|| over (dQ, dK),
+  g_R the gradient with only the last R steps differentiable; the selected
+  depth is the smallest R with eta_R below the tolerance.
 * Exact tail adjoint (section 2.2): reverse-mode through the R tail steps
   with the base held constant.  Every staircase plan P^(r,s) =
   exp(S + u^(r) (+) v^(s)) is built explicitly here (for R = 2 these are
@@ -55,6 +59,7 @@ __all__ = [
     "solve", "Solution", "output", "adjoint", "Grads",
     "forward_batch", "backward_batch", "bptt_batch", "forward_backward_batch",
     "row_marginal_error", "base_errors", "select_base_length", "converged_base_length",
+    "tail_depth_gradients", "certificate_eta", "select_tail_depth", "certificate_batch",
 ]
 
 
@@ -541,6 +546,60 @@ def forward_backward_batch(Q, K, V, a, b, W, T, R, dO, lengths=None, dustbin=Fal
             "dK": np.stack([g.dK for g in gs]).reshape(shp),
             "dV": np.stack([g.dV for g in gs]).reshape(shp),
             "vbar0": np.stack([g.vbar0 for g in gs]).reshape(B, H, L)}
+
+
+# ---------------------------------------------------------------------------
+# A-posteriori certificate of the stop-gradient bias (section 2.4, third
+# certificate; section 4.1: it picks the smallest tail depth within a tolerance)
+# ---------------------------------------------------------------------------
+
+def tail_depth_gradients(q, k, vv, a, b, sup: Support, T: int, R_max: int, dO) -> List[Grads]:
+    """grads[R], R = 0..R_max: the exact gradient of one and the same forward
+    of N = T + R_max steps when only its last R steps are differentiable (the
+    stop-gradient moved to step N - R)."""
+    N = T + R_max
+    return [backward_one(q, k, vv, a, b, sup, N - R, R, dO) for R in range(R_max + 1)]
+
+
+def certificate_eta(grads: Sequence[Sequence[Grads]]) -> List[float]:
+    """eta[R] = ||g_Rmax - g_R|| / ||g_Rmax|| over (dQ, dK) of a whole batch;
+    grads[p][R] are the depth-R gradients of problem p."""
+    R_max = len(grads[0]) - 1
+    den = sum(float(np.sum(g[R_max].dQ ** 2) + np.sum(g[R_max].dK ** 2)) for g in grads)
+    eta = []
+    for R in range(R_max + 1):
+        num = sum(float(np.sum((g[R].dQ - g[R_max].dQ) ** 2) + np.sum((g[R].dK - g[R_max].dK) ** 2))
+                  for g in grads)
+        eta.append(math.sqrt(num / den) if den > 0 else (math.inf if num > 0 else 0.0))
+    return eta
+
+
+def select_tail_depth(eta: Sequence[float], tau: float) -> int:
+    """The smallest depth R with eta[R] < tau (the deepest when none is)."""
+    for R, e in enumerate(eta):
+        if e < tau:
+            return R
+    return len(eta) - 1
+
+
+def _job_depths(args):
+    q, k, vv, a, b, L, n, W, dustbin, T, R_max, dO = args
+    return tail_depth_gradients(q, k, vv, a, b, Support.build(L, n, W, dustbin), T, R_max, dO)
+
+
+def certificate_batch(Q, K, V, a, b, W, T, R_max, dO, lengths=None, dustbin=False,
+                      processes: Optional[int] = None):
+    """(eta, gradients at depth R_max as a dict of [B, H, L, d] arrays)."""
+    B, H, L, d = Q.shape
+    ns = _lengths_of(L, lengths, B)
+    jobs = [(Q[bi, h], K[bi, h], V[bi, h], a[bi], b[bi], L, ns[bi], W, dustbin, T, R_max, dO[bi, h])
+            for bi in range(B) for h in range(H)]
+    gs = _map(_job_depths, jobs, processes)
+    shp = (B, H, L, d)
+    ref = {"dQ": np.stack([g[R_max].dQ for g in gs]).reshape(shp),
+           "dK": np.stack([g[R_max].dK for g in gs]).reshape(shp),
+           "dV": np.stack([g[R_max].dV for g in gs]).reshape(shp)}
+    return certificate_eta(gs), ref
 
 
 def bptt_batch(Q, K, V, a, b, W, T, R, dO, lengths=None, dustbin=False,

@@ -48,6 +48,10 @@ MUTANTS = {
                                   "rs = pb.col_sums(pb.plan(u, v))"),
     "base check before the column update": ("        v = pb.V(u)\n        if c % every == 0",
                                             "        if c % every == 0"),
+    "certificate moves the forward": ("return [backward_one(q, k, vv, a, b, sup, N - R, R, dO)",
+                                      "return [backward_one(q, k, vv, a, b, sup, T, R, dO)"),
+    "certificate ignores dK": ("num = sum(float(np.sum((g[R].dQ - g[R_max].dQ) ** 2) + np.sum((g[R].dK - g[R_max].dK) ** 2))",
+                               "num = sum(float(np.sum((g[R].dQ - g[R_max].dQ) ** 2))"),
 }
 
 
@@ -124,6 +128,20 @@ def _checks(m):
         want = np.abs(refs.plan_dense(X, us[0], vs[0]).sum(axis=1)[:n] - a[:n]).sum()
         ok = ok and c in got and abs(got[c] - want) <= 1e-12 * max(1.0, want)
     yield "base check", ok
+    # certificate with T = 0: eta against full BPTT
+    p = workloads.custom(B=1, H=1, L=12, d=3, W=5, T=0, R=3, seed=4, scale=1.2)
+    q, k, vv, dO = p.Q[0, 0], p.K[0, 0], p.V[0, 0], p.dO[0, 0]
+    a, b = _random_marginals(p, 5)
+    sup = m.Support.build(12, 12, 5)
+    eta = m.certificate_eta([m.tail_depth_gradients(q, k, vv, a, b, sup, 0, 3, dO)])
+    mask = refs.support_mask(12, 12, 5)
+    fq, fk, _, _ = refs.torch_surrogate_grads(q, k, vv, a, b, mask, 0, 3, dO, detach_base=False)
+    ok = True
+    for R in range(3):
+        tq, tk, _, _ = refs.torch_surrogate_grads(q, k, vv, a, b, mask, 3 - R, R, dO)
+        want = math.sqrt((np.sum((tq - fq) ** 2) + np.sum((tk - fk) ** 2)) / (np.sum(fq ** 2) + np.sum(fk ** 2)))
+        ok = ok and abs(eta[R] - want) <= 1e-9 * want
+    yield "certificate", ok
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -448,3 +448,79 @@ def test_select_base_length_rule():
     assert oracle.select_base_length([e1, e2], 9, 1e-9) == 9
     assert oracle.select_base_length([e1, {2: float("nan"), 4: 0.0, 6: 0.0}], 9, 1.0) == 4
     assert oracle.select_base_length([{}], 3, 1.0) == 3
+
+
+# --- a-posteriori bias certificate (section 2.4, third certificate) -------------
+
+def _torch_base_vjp(q, k, a, b, mask, M, seed):
+    """Gradient w.r.t. (q, k) of <seed, v^(M)>, v^(M) the column potential
+    after M Sinkhorn steps from zero, by torch float64 autograd through the
+    unrolled dense iteration (independent of the oracle)."""
+    import torch
+    dt = torch.float64
+    Q = torch.tensor(np.asarray(q, np.float64), dtype=dt, requires_grad=True)
+    K = torch.tensor(np.asarray(k, np.float64), dtype=dt, requires_grad=True)
+    Mk = torch.tensor(mask)
+    X = torch.where(Mk, Q @ K.T / math.sqrt(q.shape[1]), torch.tensor(-1e200, dtype=dt))
+    la = torch.log(torch.tensor(np.asarray(a, np.float64), dtype=dt))
+    lb = torch.log(torch.tensor(np.asarray(b, np.float64), dtype=dt))
+    L = q.shape[0]
+    u = torch.zeros(L, dtype=dt)
+    v = torch.zeros(L, dtype=dt)
+    for _ in range(M):
+        u = la - torch.logsumexp(X + v[None, :], dim=1)
+        v = lb - torch.logsumexp(X + u[:, None], dim=0)
+    (v * torch.tensor(np.asarray(seed, np.float64), dtype=dt)).sum().backward()
+    return Q.grad.numpy(), K.grad.numpy()
+
+
+@pytest.mark.parametrize("R,dust", [(1, False), (2, False), (2, True)])
+def test_discarded_adjoint_reconstructs_full_residual(R, dust):
+    """The full gradient minus the depth-R surrogate gradient is exactly the
+    discarded adjoint vbar0 pulled back through the stopped base (what the
+    certificate measures; section 4.1 reports this reconstruction)."""
+    L, W, N = 14, 5, 7
+    n = L - 1 if dust else L
+    p = workloads.custom(B=1, H=1, L=L, d=4, W=W, T=N - R, R=R, lengths=[n] if dust else None,
+                         dustbin=dust, seed=21, scale=1.2)
+    q, k, vv, a, b, dO = p.Q[0, 0], p.K[0, 0], p.V[0, 0], p.a[0], p.b[0], p.dO[0, 0]
+    sup = oracle.Support.build(L, n, W, dust)
+    tail = oracle.backward_one(q, k, vv, a, b, sup, N - R, R, dO)
+    full = oracle.bptt_one(q, k, vv, a, b, sup, N - R, R, dO)
+    mask = refs.support_mask(L, n, W, dust)
+    gq, gk = _torch_base_vjp(q, k, a, b, mask, N - R, np.where(np.isfinite(tail.vbar0), tail.vbar0, 0))
+    assert _rel(full.dQ - tail.dQ, gq) < 1e-10
+    assert _rel(full.dK - tail.dK, gk) < 1e-10
+    assert np.linalg.norm(gq) > 1e-6 * np.linalg.norm(full.dQ)  # a non-trivial residual
+
+
+def test_certificate_without_base_is_the_full_residual():
+    """T = 0: the deepest tail is full BPTT, so eta_R is exactly
+    ||g_BPTT - g_R|| / ||g_BPTT|| over (dQ, dK)."""
+    p = workloads.custom(B=1, H=2, L=20, d=4, W=7, T=0, R=5, seed=8, scale=1.1)
+    grads, fulls = [], []
+    for h in range(2):
+        q, k, vv, a, b, dO = p.Q[0, h], p.K[0, h], p.V[0, h], p.a[0], p.b[0], p.dO[0, h]
+        sup = oracle.Support.build(p.L, p.L, p.W)
+        grads.append(oracle.tail_depth_gradients(q, k, vv, a, b, sup, 0, 5, dO))
+        fulls.append(oracle.bptt_one(q, k, vv, a, b, sup, 0, 5, dO))
+    eta = oracle.certificate_eta(grads)
+    den = sum(np.sum(f.dQ ** 2) + np.sum(f.dK ** 2) for f in fulls)
+    for R in range(6):
+        num = sum(np.sum((g[R].dQ - f.dQ) ** 2) + np.sum((g[R].dK - f.dK) ** 2)
+                  for g, f in zip(grads, fulls))
+        assert abs(eta[R] - math.sqrt(num / den)) <= 1e-12 + 1e-9 * eta[R], (R, eta[R])
+    assert eta[5] == 0.0
+
+
+def test_certificate_decays_with_depth():
+    """Section 2.4 (first certificate): the surrogate bias shrinks
+    geometrically with the tail depth on a contractive problem."""
+    p = workloads.make(1)
+    q, k, vv, a, b = _one(p)
+    g = oracle.tail_depth_gradients(q, k, vv, a, b, oracle.Support.build(p.L, p.L, p.W), 16, 4,
+                                    p.dO[0, 0])
+    eta = oracle.certificate_eta([g])
+    assert all(eta[R + 1] < 0.9 * eta[R] for R in range(3)), eta
+    assert oracle.select_tail_depth(eta, math.sqrt(eta[1] * eta[2])) == 2
+    assert oracle.select_tail_depth(eta, 0.0) == 4
