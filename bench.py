@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--certificate-rmax", type=int, default=4,
                     help="also time the stop-gradient bias certificate up to this depth (0: skip)")
     ap.add_argument("--certificate-tau", type=float, default=1e-5)
+    ap.add_argument("--contraction-block", type=int, default=128,
+                    help="also time the projective contraction diagnostic at this block size (0: skip)")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
@@ -373,6 +375,20 @@ def main():
                        "ms": round(c_ms, 3), "timing": "host clock, one call (R_max + 1 backward passes)"}
         del Oc, wsc
 
+    # Projective contraction diagnostic over the diagonal band blocks.
+    contraction = None
+    if args.contraction_block > 0:
+        blk = args.contraction_block
+        eoba.block_contraction(Q, K, W, blk)  # warm
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        cev[0].record(stream)
+        delta, kappa = eoba.block_contraction(Q, K, W, blk)
+        cev[1].record(stream)
+        torch.cuda.synchronize()
+        contraction = {"block": blk, "blocks": int(kappa.numel()), "delta_max": round(float(delta.max()), 4),
+                       "kappa_max": round(float(kappa.max()), 4), "kappa_mean": round(float(kappa.mean()), 4),
+                       "ms": round(cev[0].elapsed_time(cev[1]), 4)}
+
     if args.copy_calibration:
         x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         y = torch.empty_like(x)
@@ -422,6 +438,8 @@ def main():
         out["converged_base"] = converged
     if certificate is not None:
         out["certificate"] = certificate
+    if contraction is not None:
+        out["contraction"] = contraction
     if not args.no_cpu_baseline:
         cb = cpu_baseline(prob, args.cpu_heads)
         cb.pop("seconds", None)

@@ -25,7 +25,8 @@ SINKATTN_F32 = 0
 SINKATTN_BF16 = 1
 
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
-            "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate", "sinkattn_timing_enable", "sinkattn_timing_collect",
+            "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate",
+            "sinkattn_block_contraction", "sinkattn_timing_enable", "sinkattn_timing_collect",
             "sinkattn_status_string", "sinkattn_version")
 
 
@@ -72,6 +73,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_tail_certificate.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, sz,
                                               vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_double), vp]
     lib.sinkattn_tail_certificate.restype = i32
+    lib.sinkattn_block_contraction.argtypes = [vp, vp, i32, shp, i32, vp, vp, vp]
+    lib.sinkattn_block_contraction.restype = i32
     lib.sinkattn_timing_enable.argtypes = [i32]
     lib.sinkattn_timing_enable.restype = i32
     lib.sinkattn_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -289,6 +292,30 @@ def tail_certificate(Q, K, V, W: int, T: int, R_max: int, a, b, O, dO, workspace
         _stream(Q.device))
     _check(st)
     return dQ, dK, dV, [float(x) for x in eta]
+
+
+def block_contraction(Q, K, W: int, block: int, lengths=None, dustbin: bool = False):
+    """Hilbert projective diameter Delta of every diagonal band block of size
+    `block` (see sinkattn_block_contraction).  Returns (delta, kappa), device
+    fp32 tensors [B, H, ceil(L / block)]; kappa = tanh(delta / 4) is the
+    block's contraction coefficient."""
+    torch = _torch()
+    if Q.dim() != 4 or K.shape != Q.shape or K.dtype != Q.dtype:
+        raise ValueError("Q and K must be [B, H, L, d] of one dtype")
+    if not (Q.is_contiguous() and K.is_contiguous()):
+        raise ValueError("Q and K must be contiguous")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.device != Q.device):
+        raise ValueError("lengths must be an int32 tensor on Q's device")
+    shape = _shape_of(Q, lengths, dustbin)
+    B, H, L, _ = Q.shape
+    nblk = (L + block - 1) // block if block > 0 else 1  # the library rejects block < 1
+    delta = torch.empty((B, H, nblk), dtype=torch.float32, device=Q.device)
+    kappa = torch.empty_like(delta)
+    s = shape.c()
+    st = load_library().sinkattn_block_contraction(_ptr(Q), _ptr(K), W, ctypes.byref(s), block, _ptr(delta),
+                                                   _ptr(kappa), _stream(Q.device))
+    _check(st)
+    return delta, kappa
 
 
 def select_tail_depth(eta, tau: float) -> int:

@@ -16,6 +16,8 @@ namespace sinkattn {
 
 hipError_t launch_forward(const Geom& g, int dtype, const FwdLaunch& f, const Workspace& w, hipStream_t st);
 hipError_t launch_backward(const Geom& g, int dtype, const BwdLaunch& f, const Workspace& w, hipStream_t st);
+hipError_t launch_block_diameters(const Geom& g, int dtype, const void* Q, const void* K, int Bd, float* delta,
+                                  float* kappa, hipStream_t st);
 hipError_t launch_certificate(const Geom& g, int dtype, const BwdLaunch& base, int R_max, const Workspace& w,
                               float* dQs, float* dKs, double* eta, hipStream_t st);
 
@@ -283,6 +285,20 @@ int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W
   if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
   BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, nullptr, T, R_max};
   hipError_t e = launch_certificate(g, s->dtype, f, R_max, w, dQ_scratch, dK_scratch, eta, stream);
+  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
+  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+}
+
+int sinkattn_block_contraction(const void* Q, const void* K, int W, const sinkattn_shape* s, int block,
+                               float* delta, float* kappa, hipStream_t stream) {
+  if (!Q || !K || !delta) return SINKATTN_EINVAL;
+  Geom g;
+  int st = make_geom(s, W, &g);
+  if (st != SINKATTN_OK) return st;
+  // the block must lie wholly inside the band (a strictly positive kernel)
+  const int inside = (g.h1 < g.h2 ? g.h1 : g.h2) + 1;
+  if (block < 1 || block > 128 || block > inside) return SINKATTN_EINVAL;
+  hipError_t e = launch_block_diameters(g, s->dtype, Q, K, block, delta, kappa, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
   return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
 }

@@ -193,6 +193,25 @@ int sinkattn_tail_certificate(const void *Q, const void *K, const void *V, int W
                               float *dV, float *dQ_scratch, float *dK_scratch, double *eta,
                               hipStream_t stream);
 
+/* Projective contraction diagnostic (section 2.4, second certificate): the
+ * Hilbert projective diameter of every diagonal band block.  Blocks are
+ * [s, s + block) x [s, s + block) over the real tokens of each sequence
+ * (s = 0, block, 2 block, ...; the last one clipped to n_b; the dustbin is
+ * not part of any block).  With block <= min(floor(W/2), ceil(W/2) - 1) + 1
+ * every block lies inside the band, so its kernel exp(S) is strictly
+ * positive and contracts Hilbert's projective metric by
+ * kappa = tanh(Delta / 4) < 1 (Birkhoff-Hopf), where
+ *   Delta = max over i, j, k, l in the block of S_ik + S_jl - S_jk - S_il
+ * (S = q.k / sqrt(d), natural log units); one Sinkhorn step restricted to
+ * the block contracts by at most kappa^2.
+ *   block  : 1 .. 128 and inside the band as above, else SINKATTN_EINVAL.
+ *   delta  : out, device fp32 [B, H, ceil(L / block)]: Delta per block
+ *            (0 for blocks past n_b and for one-token blocks).
+ *   kappa  : optional out (may be NULL), same shape: tanh(Delta / 4).
+ * Stream-ordered; returns before anything is enqueued on bad arguments. */
+int sinkattn_block_contraction(const void *Q, const void *K, int W, const sinkattn_shape *s,
+                               int block, float *delta, float *kappa, hipStream_t stream);
+
 /* Diagnostics for benchmarking: timing of the fused Sinkhorn step kernel,
  * which dominates the run time.  While enabled (on != 0), sinkattn_forward
  * records HIP events on the caller's stream around its step-kernel launches:

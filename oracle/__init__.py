@@ -19,6 +19,6 @@ from .sinkhorn import (  # noqa: F401
 from .sinkhorn import _Problem as Problem  # noqa: F401
 from .sinkhorn import backward_one, bptt_one, forward_one  # noqa: F401
 from .sinkhorn import (  # noqa: F401
-    base_errors, certificate_batch, certificate_eta, converged_base_length, row_marginal_error,
+    base_errors, block_contraction_batch, block_diameters, certificate_batch, certificate_eta, converged_base_length, row_marginal_error,
     select_base_length, select_tail_depth, tail_depth_gradients,
 )

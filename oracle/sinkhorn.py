@@ -28,6 +28,9 @@ design notes):
   sum_i |sum_j P^(c,c)_ij - a_i|, checked every k steps; a batch stops at the
   first check where every problem is below the tolerance.
 * Output: P = exp(S + u^(R) (+) v^(R)) on Omega, O = P V.
+* Contraction diagnostic (section 2.4, second certificate): the Hilbert
+  projective diameter Delta of each diagonal band block (strictly positive
+  kernel), whose Birkhoff contraction coefficient is tanh(Delta / 4).
 * Bias certificate (section 2.4, third certificate): for one forward of
   N = T + R_max steps, eta_R = ||g_Rmax - g_R|| / ||g_Rmax|| over (dQ, dK),
   g_R the gradient with only the last R steps differentiable; the selected
@@ -60,6 +63,7 @@ __all__ = [
     "forward_batch", "backward_batch", "bptt_batch", "forward_backward_batch",
     "row_marginal_error", "base_errors", "select_base_length", "converged_base_length",
     "tail_depth_gradients", "certificate_eta", "select_tail_depth", "certificate_batch",
+    "block_diameters", "block_contraction_batch",
 ]
 
 
@@ -600,6 +604,44 @@ def certificate_batch(Q, K, V, a, b, W, T, R_max, dO, lengths=None, dustbin=Fals
            "dK": np.stack([g[R_max].dK for g in gs]).reshape(shp),
            "dV": np.stack([g[R_max].dV for g in gs]).reshape(shp)}
     return certificate_eta(gs), ref
+
+
+# ---------------------------------------------------------------------------
+# Projective contraction diagnostic (section 2.4, second certificate: Hilbert's
+# projective metric shows that strictly positive active blocks contract)
+# ---------------------------------------------------------------------------
+
+def block_diameters(q, k, L: int, n: int, W: int, block: int) -> np.ndarray:
+    """Hilbert projective diameter of each diagonal block [s, s + block) of the
+    n real tokens (s = 0, block, ...; the last clipped to n; 0 past n):
+    Delta = max over i, j, k, l of S_ik + S_jl - S_jk - S_il, the largest log
+    cross-ratio of the block's kernel exp(S).  The block must lie inside the
+    band (block <= min(h1, h2) + 1), where that kernel is strictly positive;
+    its Birkhoff contraction coefficient is tanh(Delta / 4)."""
+    h1, h2 = band_offsets(W)
+    if not 1 <= block <= min(h1, h2) + 1:
+        raise ValueError("block must lie inside the band")
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    d = q.shape[1]
+    out = np.zeros((L + block - 1) // block)
+    for blk, s in enumerate(range(0, L, block)):
+        if s >= n:
+            continue
+        e = min(s + block, n)
+        S = q[s:e] @ k[s:e].T / math.sqrt(d)
+        diff = S[:, None, :] - S[None, :, :]  # [i, j, k]: S_ik - S_jk
+        M = diff.max(axis=2)                   # max over k
+        out[blk] = float((M + M.T).max())      # + max over l of S_jl - S_il
+    return out
+
+
+def block_contraction_batch(Q, K, W, block, lengths=None):
+    """block_diameters for every (b, h): [B, H, ceil(L / block)]."""
+    B, H, L, d = Q.shape
+    ns = _lengths_of(L, lengths, B)
+    return np.stack([np.stack([block_diameters(Q[bi, h], K[bi, h], L, ns[bi], W, block)
+                               for h in range(H)]) for bi in range(B)])
 
 
 def bptt_batch(Q, K, V, a, b, W, T, R, dO, lengths=None, dustbin=False,

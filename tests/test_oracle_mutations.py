@@ -50,6 +50,8 @@ MUTANTS = {
                                             "        if c % every == 0"),
     "certificate moves the forward": ("return [backward_one(q, k, vv, a, b, sup, N - R, R, dO)",
                                       "return [backward_one(q, k, vv, a, b, sup, T, R, dO)"),
+    "diameter without the transpose": ("out[blk] = float((M + M.T).max())", "out[blk] = float((M + M).max())"),
+    "diameter over rows only": ("M = diff.max(axis=2)", "M = diff.max(axis=1)"),
     "certificate ignores dK": ("num = sum(float(np.sum((g[R].dQ - g[R_max].dQ) ** 2) + np.sum((g[R].dK - g[R_max].dK) ** 2))",
                                "num = sum(float(np.sum((g[R].dQ - g[R_max].dQ) ** 2))"),
 }
@@ -142,6 +144,18 @@ def _checks(m):
         want = math.sqrt((np.sum((tq - fq) ** 2) + np.sum((tk - fk) ** 2)) / (np.sum(fq ** 2) + np.sum(fk ** 2)))
         ok = ok and abs(eta[R] - want) <= 1e-9 * want
     yield "certificate", ok
+    # contraction diagnostic: brute-force cross ratios
+    rng = np.random.default_rng(12)
+    qd, kd = rng.normal(size=(9, 3)), rng.normal(size=(9, 3))
+    got = m.block_diameters(qd, kd, 9, 9, 9, 4)
+    ok = True
+    for b_, s0 in enumerate(range(0, 9, 4)):
+        e0 = min(s0 + 4, 9)
+        S = qd[s0:e0] @ kd[s0:e0].T / math.sqrt(3)
+        best = max(S[i, kk] + S[j, ll] - S[j, kk] - S[i, ll] for i in range(e0 - s0) for j in range(e0 - s0)
+                   for kk in range(e0 - s0) for ll in range(e0 - s0))
+        ok = ok and abs(got[b_] - best) < 1e-12
+    yield "diameter", ok
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -524,3 +524,63 @@ def test_certificate_decays_with_depth():
     assert all(eta[R + 1] < 0.9 * eta[R] for R in range(3)), eta
     assert oracle.select_tail_depth(eta, math.sqrt(eta[1] * eta[2])) == 2
     assert oracle.select_tail_depth(eta, 0.0) == 4
+
+
+# --- projective contraction diagnostic (section 2.4, second certificate) ------
+
+def _hilbert(x, y):
+    r = np.log(x) - np.log(y)
+    return r.max() - r.min()
+
+
+def test_block_diameter_brute_force():
+    """Delta equals the largest log cross-ratio over all index quadruples."""
+    rng = np.random.default_rng(2)
+    L, n, W, blk, d = 13, 11, 12, 5, 3
+    q = rng.normal(size=(L, d))
+    k = rng.normal(size=(L, d))
+    got = oracle.block_diameters(q, k, L, n, W, blk)
+    assert got.shape == (3,)
+    for b_, s in enumerate(range(0, L, blk)):
+        e = min(s + blk, n)
+        best = 0.0
+        for i in range(s, e):
+            for j in range(s, e):
+                for kk in range(s, e):
+                    for ll in range(s, e):
+                        x = (q[i] @ k[kk] + q[j] @ k[ll] - q[j] @ k[kk] - q[i] @ k[ll]) / math.sqrt(d)
+                        best = max(best, x)
+        assert abs(got[b_] - best) < 1e-12, (b_, got[b_], best)
+
+
+def test_block_diameter_closed_forms():
+    """A rank-one kernel (S_ik = f_i + g_k) has diameter 0; a 2 x 2 block has
+    |S_11 + S_22 - S_12 - S_21|."""
+    rng = np.random.default_rng(4)
+    f, g = rng.normal(size=8), rng.normal(size=8)
+    q = np.stack([f, np.ones(8)], axis=1) * math.sqrt(2)
+    k = np.stack([np.ones(8), g], axis=1)
+    assert np.all(np.abs(oracle.block_diameters(q, k, 8, 8, 17, 8)) < 1e-12)
+    q2, k2 = rng.normal(size=(2, 4)), rng.normal(size=(2, 4))
+    S = q2 @ k2.T / 2.0
+    got = oracle.block_diameters(q2, k2, 2, 2, 3, 2)[0]
+    assert abs(got - abs(S[0, 0] + S[1, 1] - S[0, 1] - S[1, 0])) < 1e-12
+
+
+def test_block_contraction_birkhoff():
+    """Birkhoff-Hopf: the block kernel contracts Hilbert's projective metric by
+    tanh(Delta / 4), and not by much less (random pairs come close)."""
+    rng = np.random.default_rng(6)
+    d, blk = 4, 6
+    q, k = rng.normal(size=(blk, d)) * 0.7, rng.normal(size=(blk, d)) * 0.7
+    delta = oracle.block_diameters(q, k, blk, blk, 2 * blk + 1, blk)[0]
+    kappa = math.tanh(delta / 4)
+    Kmat = np.exp(q @ k.T / math.sqrt(d))
+    worst = 0.0
+    for _ in range(4000):
+        x = np.exp(rng.normal(size=blk) * 3)
+        y = np.exp(rng.normal(size=blk) * 3)
+        ratio = _hilbert(Kmat @ x, Kmat @ y) / _hilbert(x, y)
+        assert ratio <= kappa + 1e-12
+        worst = max(worst, ratio)
+    assert 0.0 < kappa < 1.0 and worst > 0.5 * kappa
