@@ -187,18 +187,20 @@ __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, 
 
 // One launch = one Sinkhorn step over every (b, h).  A workgroup sweeps a
 // segment of SB consecutive 128-row blocks of one sequence:
-//  * the K window of a block (NWT tiles of 16 rows) lives in an LDS ring that
-//    slides by 8 tiles per block; each LDS row holds the K row followed by
-//    four copies of w_j = v^(t-1)_j - vref, so a lane reads its tile operand
-//    and its column's w at one address;
+//  * the K window of a block (NWT tiles of 16 rows) lives in an LDS ring of
+//    NWT + 8 tiles that slides by 8 tiles per block; w_j = v^(t-1)_j - vref
+//    of each ring column sits in a separate array (a tile's four lanes per
+//    column read one word);
 //  * each wave computes one 16-row strip per block; its column partials go
 //    to a per-wave buffer (two buffers, alternating by block), and the fold of
 //    block k-1's partials into the segment's column sums runs during block k,
 //    off the barrier-to-barrier path; a column's sum is written once, when
 //    the column leaves the window;
 //  * the next block's K rows, Q strips, a_i and column-finish inputs are
-//    loaded into registers while the current block computes; the strip issues
-//    no global loads, so those loads stay in flight.
+//    loaded into registers while the current block computes (the strip issues
+//    no global loads, so those loads stay in flight), and its 8 new K tiles go
+//    to the ring's 8 spare slots as soon as a wave's strip is done, so one
+//    barrier per block suffices.
 // NT (tiles per strip) and the ring size are compile-time; tiles that cross
 // the band edge (a host-computed bit mask) or strips with non-real rows are
 // masked per entry.
@@ -206,12 +208,15 @@ template <typename T, int D, int NT>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
   constexpr int NCH = RB / 64;             // 16-byte lane chunks per row
-  constexpr int RS = RB + 80;              // LDS row: K row, w copies at RB + 16 c, pad
+  constexpr int RS = RB + 16;              // LDS row: K row + 16 bytes (conflict-free lane reads)
   constexpr int TILEB = 16 * RS;           // bytes per ring tile
   constexpr int PER_ROW = RB / 16;         // 16-byte chunks per row
   constexpr int NEWLD = (kBlockRows * PER_ROW + 511) / 512;  // chunks per thread per block
-  constexpr int NWT = NT + kWaves - 1;     // ring tiles = window of one block
+  constexpr int NWT = NT + kWaves - 1;     // window tiles of one block
   constexpr int NWC = NWT * 16;
+  constexpr int RING = NWT + 8;            // ring tiles: the window + the next block's 8 new tiles
+  constexpr int NRC = RING * 16;           // ring columns
+  constexpr int CBW = NT * 16;             // per-wave partials: one per strip column
   constexpr int kThreads = 512;            // launch size (a constant: reading blockDim.x is a memory load)
   static_assert(kBlockRows * PER_ROW == NEWLD * kThreads, "whole 16-byte chunks per thread");
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -236,10 +241,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   const int seg_r0 = b0 * kBlockRows;
   const int seg_r1 = seg_r0 + g.SB * kBlockRows;  // owned columns [seg_r0, seg_r1)
   const int cs = seg_r0 - 16 * g.TL;              // first column of the segment window
-  char* kw = smem;                                                     // [NWC][RS] ring
-  float* colsum = reinterpret_cast<float*>(smem + (size_t)NWC * RS);  // [NWC] segment sums
-  float* colbuf = colsum + NWC;                                        // [2][8][NWC] partials
-  float* misc = colbuf + 2 * kWaves * NWC;                             // [2][8] dustbin partials
+  char* kw = smem;                                                     // [NRC][RS] K ring
+  float* wv = reinterpret_cast<float*>(smem + (size_t)NRC * RS);      // [NRC] w_j = v_j - vref
+  float* colsum = wv + NRC;                                            // [NRC] segment sums
+  float* colbuf = colsum + NRC;                                        // [2][8][CBW] partials
+  float* misc = colbuf + 2 * kWaves * CBW;                             // [2][8] dustbin partials
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -259,15 +265,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       if (p.v_tail) p.v_tail[bh * L + j] = vj;
     }
   };
-  auto wrap = [](int x) { return x >= NWT ? x - NWT : x; };  // x in [0, 2 NWT)
-  // the four copies of w in LDS row c (ring slot c / 16)
-  auto put_w = [&](int c, float w) {
-    float* row = reinterpret_cast<float*>(kw + (size_t)c * RS + RB);
-    row[0] = w;
-    row[4] = w;
-    row[8] = w;
-    row[12] = w;
-  };
+  auto wrap = [](int x) { return x >= RING ? x - RING : x; };  // x in [0, 2 RING)
+  // w of ring column c (the four lanes of a tile column read one word)
+  auto put_w = [&](int c, float w) { wv[c] = w; };
 
   // prologue: window of block b0 in ring slots 0 .. NWT-1.  All loads are
   // issued before any is used (one memory round trip, not one per row group).
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         w = (float)(vj - vref);
       }
       put_w(tid, w);
-      colsum[tid] = 0.f;
     }
+    for (int c = tid; c < NRC; c += kThreads) colsum[c] = 0.f;
 #pragma unroll
     for (int e = 0; e < PRO; ++e) {
       const int idx = tid + e * kThreads;
@@ -345,18 +345,19 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   // slot rbf) into the segment sums in wave order; write out the columns
   // that leave the window after block kf (all of them when `last`).
   auto fold = [&](int kf, int bf, int rbf, bool last) {
-    for (int c = tid; c < NWC; c += kThreads) {
-      int off = (c >> 4) - rbf;  // tile offset within block kf's window
-      off = off < 0 ? off + NWT : off;
+    for (int wc = tid; wc < NWC; wc += kThreads) {
+      const int off = wc >> 4;                         // tile offset within block kf's window
+      const int c = wrap(rbf + off) * 16 + (wc & 15);  // its ring column
       float s = colsum[c];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const bool wrote = off >= w && off < w + NT && kf * kBlockRows + 16 * w < n;
-        const float x = colbuf[(bf * kWaves + w) * NWC + c];
+        const int lt = off - w;  // the tile's index in wave w's strip
+        const bool wrote = lt >= 0 && lt < NT && kf * kBlockRows + 16 * w < n;
+        const float x = colbuf[(bf * kWaves + w) * CBW + (wrote ? lt : 0) * 16 + (wc & 15)];
         s += wrote ? x : 0.f;
       }
       if (off < 8 || last) {
-        const int j = (kf * 8 - g.TL + off) * 16 + (c & 15);
+        const int j = (kf * 8 - g.TL + off) * 16 + (wc & 15);
         p.part_out[((size_t)bh * g.nseg + seg) * g.SW + (j - cs)] = s;
         s = 0.f;
       }
@@ -370,6 +371,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   };
 
   const char* lane_k = kw + lr * RS + lg * 16;  // lane's operand bytes in ring row lr
+  const float* lane_wv = wv + lr;               // w of the lane's tile column
   int jpend = -1;                               // entering column whose v is not yet stored
   double vpend = 0.0;
   auto flush_pending = [&]() {
@@ -464,10 +466,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         }
       };
       auto read_tile = [&](int t, u4 (&kb)[NCH], float& w) {
-        const char* src = lane_k + wrap(sw + t) * TILEB;
+        const int sl = wrap(sw + t);
+        const char* src = lane_k + sl * TILEB;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) kb[c] = ld16(src + c * 64);
-        w = *reinterpret_cast<const float*>(src + RB);
+        w = lane_wv[sl * 16];
       };
       auto mma_tile = [&](const u4 (&kb)[NCH]) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       }
       // column partials of this strip, sum_i e_ij h_i, reduced over the four
       // lane rows four tiles at a time (row g ends with tile t + g's sums)
-      float* cb = colbuf + (buf * kWaves + wave) * NWC;
+      float* cb = colbuf + (buf * kWaves + wave) * CBW;  // indexed by strip column
       auto colp = [&](int t) {
         float cp = e[t][0] * h[0];
         cp = __builtin_fmaf(e[t][1], h[1], cp);
@@ -619,12 +622,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
 #pragma unroll
       for (int t = 0; t + 3 < NT; t += 4) {
         const float s4 = cross_row_sum4(colp(t), colp(t + 1), colp(t + 2), colp(t + 3));
-        cb[wrap(sw + t + lg) * 16 + lr] = s4;
+        cb[(t + lg) * 16 + lr] = s4;
       }
 #pragma unroll
       for (int t = NT & ~3; t < NT; ++t) {
         const float s1 = cross_row_sum(colp(t));
-        if (lg == 0) cb[wrap(sw + t) * 16 + lr] = s1;
+        if (lg == 0) cb[t * 16 + lr] = s1;
       }
       if (g.dustbin) {
         float dp = 0.f;
@@ -652,22 +655,26 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         wnew = (float)(vj - vref);
       }
     }
-    __syncthreads();
     if (more) {
-      // ---- the new tiles take the ring slots rb .. rb + 7 that block k freed
+      // ---- the new tiles take ring slots rb + NWT .. rb + NWT + 7, which no
+      // strip of block k reads (block k - 1's first tiles left them), so each
+      // wave stores its share as soon as its own strip is done: one barrier
+      // per block
 #pragma unroll
       for (int e = 0; e < NEWLD; ++e) {
         const int idx = tid + e * 512;
         const int row = idx / PER_ROW;
         const int j = jn0 + row;
         const u4 val = j < n ? knew[e] : (u4){0u, 0u, 0u, 0u};
-        st16(kw + (size_t)(wrap(rb + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, val);
+        st16(kw + (size_t)(wrap(rb + NWT + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, val);
       }
-      if (tid < kBlockRows) put_w(wrap(rb + (tid >> 4)) * 16 + (tid & 15), wnew);
+      if (tid < kBlockRows) put_w(wrap(rb + NWT + (tid >> 4)) * 16 + (tid & 15), wnew);
+    }
+    __syncthreads();
+    if (more) {
       cur = nxt;
       rbp = rb;
       rb = wrap(rb + 8);
-      __syncthreads();
     }
   }
   flush_pending();
@@ -1320,7 +1327,9 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   const size_t BHL = (size_t)nbh * g.L;
   const int grid = padded8(nbh * g.nblk);
   const int iter_grid = padded8(nbh * g.nseg);
-  const size_t iter_lds = (size_t)g.NWC * (RB + 80) + (size_t)g.NWC * 4 * (1 + 2 * kWaves) + 2 * kWaves * 4 + 64;
+  const int ring_cols = g.NWC + 8 * 16;  // window + the next block's 8 tiles
+  const size_t iter_lds = (size_t)ring_cols * (RB + 16) + (size_t)ring_cols * 4 * 2 +
+                          (size_t)2 * kWaves * g.NT * 16 * 4 + 2 * kWaves * 4 + 64;
   const size_t out_lds = (size_t)g.NWC * 4 + (size_t)D * (g.NWC + 8) * Elt<T>::kBytes + 64;
   hipError_t err;
   if (iter_lds > 160 * 1024 || out_lds > 160 * 1024) return hipErrorInvalidConfiguration;
