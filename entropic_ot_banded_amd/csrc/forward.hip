@@ -250,6 +250,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // the entering columns of a block (finish inputs, v, w) belong to the
+  // first two waves
+  const int ec = tid < kBlockRows ? tid : -1;  // entering column, valid when >= 0
   const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
   const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
   const DustC dc = load_dust(g, bh, p.dstate);
@@ -351,9 +354,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       float s = colsum[c];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const int lt = off - w;  // the tile's index in wave w's strip
+        // the tile's index in wave w's strip; the read address stays inside
+        // the buffers for every off and w (lt in [-7, NWT)), so it is affine
+        // in w and unselected values are discarded
+        const int lt = off - w;
         const bool wrote = lt >= 0 && lt < NT && kf * kBlockRows + 16 * w < n;
-        const float x = colbuf[(bf * kWaves + w) * CBW + (wrote ? lt : 0) * 16 + (wc & 15)];
+        const float x = colbuf[(bf * kWaves + w) * CBW + lt * 16 + (wc & 15)];
         s += wrote ? x : 0.f;
       }
       if (off < 8 || last) {
@@ -411,11 +417,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         load_q_chunk(kn, part - NEWLD, nxt);
       } else if (part == NEWLD + NCH) {
         load_row_scalars(kn, nxt);
-      } else if (tid < kBlockRows && p.part_in) {
-        // j + 16 TL = (k + 1) 128 + 16 (TL + TR) + tid with tid < 128, so the
+      } else if (ec >= 0 && p.part_in) {
+        // j + 16 TL = (k + 1) 128 + 16 (TL + TR) + ec with ec < 128, so the
         // first segment window holding j is (k + 1) / SB and the last is at
         // most two further (16 (TL + TR) <= 256 <= 2 segw)
-        int j = jp0 + tid;
+        int j = jp0 + ec;
         const int segw = g.SB * kBlockRows;
         const int slo = kn / g.SB;
         const int x = j + 16 * g.TL;
@@ -432,9 +438,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     const int i0 = k * kBlockRows + wave * 16;
     if (i0 < n) {
       // Store the entering columns' v from the previous block now, a whole
-      // strip before the next loop top.  (Waves 0 and 1 hold them; a strip is
-      // skipped only in the segment's last block, after which none is pending
-      // until the final flush.)
+      // strip before the next loop top.  (The first two waves hold them; a
+      // strip is skipped only in the segment's last block, after which none
+      // is pending until the final flush.)
       flush_pending();
       const int sw = wrap(rb + wave);  // ring slot of strip tile t = 0
       const bool partial = i0 + 16 > n;
@@ -646,8 +652,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     // memory during the next strip: a store still in flight at the loop top
     // would make the next block's first loads wait for it)
     float wnew = kNegInf;
-    if (more && tid < kBlockRows) {
-      const int j = jn0 + tid;
+    if (more && ec >= 0) {
+      const int j = jn0 + ec;
       if (j >= 0 && j < n) {
         const double vj = p.part_in ? finish_from(vin, dc) : 0.0;
         jpend = j;
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         const u4 val = j < n ? knew[e] : (u4){0u, 0u, 0u, 0u};
         st16(kw + (size_t)(wrap(rb + NWT + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, val);
       }
-      if (tid < kBlockRows) put_w(wrap(rb + NWT + (tid >> 4)) * 16 + (tid & 15), wnew);
+      if (ec >= 0) put_w(wrap(rb + NWT + (ec >> 4)) * 16 + (ec & 15), wnew);
     }
     __syncthreads();
     if (more) {
