@@ -489,11 +489,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       float shift[4] = {0.f, 0.f, 0.f, 0.f};
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
       float ed[4] = {0.f, 0.f, 0.f, 0.f};
-      // The fast pass always runs (it issues the prefetch slices); on the
-      // first step, or when a row sum leaves the safe range, the strip is
-      // recomputed below with exact row maxima.
+      // The fast pass runs except on the first step, which goes straight to
+      // the exact row maxima below (and issues the prefetch slices itself);
+      // when a fast row sum leaves the safe range the strip is recomputed
+      // there as well.
       bool need_safe = p.first != 0;
-      {
+      if (!need_safe) {
         // fast path: shift vref only; pipelined MFMA / exp
         auto consume = [&](int t, const f4& acc, float w) {
           float x[4];
@@ -551,7 +552,10 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
           }
           if (rowok[r]) bad |= !(rs[r] >= 0x1p-120f && rs[r] <= 0x1p120f);
         }
-        need_safe = need_safe || __any(bad);
+        need_safe = __any(bad);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NPF; ++q) prefetch(q);
       }
       if (need_safe) {
         // exact per-row maxima (first step, or entries out of range)
