@@ -347,8 +347,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   // Fold block kf's per-wave partials (buffer bf; its window starts at ring
   // slot rbf) into the segment sums in wave order; write out the columns
   // that leave the window after block kf (all of them when `last`).
+  // (threads from kBlockRows on: the first two waves handle the entering
+  // columns instead, which balances the work ahead of the block barrier)
+  static_assert(NWC <= kThreads - kBlockRows, "one window column per folding thread");
   auto fold = [&](int kf, int bf, int rbf, bool last) {
-    for (int wc = tid; wc < NWC; wc += kThreads) {
+    const int wc = tid - kBlockRows;
+    if (wc >= 0 && wc < NWC) {
       const int off = wc >> 4;                         // tile offset within block kf's window
       const int c = wrap(rbf + off) * 16 + (wc & 15);  // its ring column
       float s = colsum[c];
