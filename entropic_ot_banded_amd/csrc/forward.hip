@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
+#include <type_traits>
 #include <vector>
 
 #include "common.hpp"
@@ -101,23 +103,39 @@ __device__ __forceinline__ DustC load_dust(const Geom& g, int bh, const double* 
   return c;
 }
 
+// Loads and stores of the values other workgroups of the same launch read
+// (column partials, published v): device-scope when COH (the persistent step
+// kernel, whose steps run in one launch: no cache may serve a stale copy),
+// plain otherwise.
+template <bool COH, typename X>
+__device__ __forceinline__ X ld_shared(const X* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH, typename X>
+__device__ __forceinline__ void st_shared(X* p, X v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
 // Loads only (no arithmetic on the loaded values), so that issuing it does
 // not make the wave wait for the data.  Column j lies in the windows of the
 // segments [slo, shi].
+template <bool COH = false>
 __device__ __forceinline__ VIn gather_v_range(const Geom& g, int bh, int n, int j, int slo, int shi,
                                               const double* v_prev2, const float* part_in, const float* b,
                                               int bb, const float* sdr) {
   const size_t L = g.L;
   const int segw = g.SB * kBlockRows;
   VIn r;
-  r.vprev = v_prev2 ? v_prev2[bh * L + j] : 0.0;
+  r.vprev = v_prev2 ? ld_shared<COH>(v_prev2 + bh * L + j) : 0.0;
   r.b = b[(size_t)bb * L + j];
 #pragma unroll
   for (int k = 0; k < kMaxSeg; ++k) {
     const int sg = slo + k;
     r.part[k] = 0.f;
     if (sg <= shi && sg * segw < n)  // segments without real rows wrote nothing
-      r.part[k] = part_in[((size_t)bh * g.nseg + sg) * g.SW + (j - (sg * segw - 16 * g.TL))];
+      r.part[k] = ld_shared<COH>(part_in + ((size_t)bh * g.nseg + sg) * g.SW + (j - (sg * segw - 16 * g.TL)));
   }
   r.sdr = g.dustbin ? sdr[bh * L + j] : 0.f;
   r.valid = (2u << kMaxSeg) - 1;
@@ -128,6 +146,7 @@ __device__ __forceinline__ VIn gather_v_range(const Geom& g, int bh, int n, int 
 // its buffer (j in [0, L)); `valid` marks the partials that count.  No
 // branch and no register written before the loads, so a wave issuing them
 // in the middle of other work never waits for earlier loads.
+template <bool COH = false>
 __device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, int j, int slo, int shi,
                                                 const double* v_prev2, const float* part_in, const float* b,
                                                 int bb, const float* sdr) {
@@ -137,7 +156,7 @@ __device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, in
   // v^(t-2) = 0 when v_prev2 is null: load from `b` instead (any readable
   // address; the finish ignores it), so no branch sits before the loads
   const double* vp = v_prev2 ? v_prev2 + bh * L : reinterpret_cast<const double*>(b);
-  r.vprev = vp[v_prev2 ? j : 0];
+  r.vprev = ld_shared<COH>(vp + (v_prev2 ? j : 0));
   r.b = b[(size_t)bb * L + j];
   r.valid = v_prev2 ? 1u << kMaxSeg : 0u;
 #pragma unroll
@@ -147,7 +166,7 @@ __device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, in
     const int sgc = sg < g.nseg ? sg : g.nseg - 1;
     int off = j - (sgc * segw - 16 * g.TL);
     off = off < 0 ? 0 : (off >= g.SW ? g.SW - 1 : off);
-    r.part[k] = part_in[((size_t)bh * g.nseg + sgc) * g.SW + off];
+    r.part[k] = ld_shared<COH>(part_in + ((size_t)bh * g.nseg + sgc) * g.SW + off);
     r.valid |= (ok ? 1u : 0u) << k;
   }
   r.sdr = sdr[bh * L + j];  // always allocated; used only with a dustbin
@@ -155,15 +174,21 @@ __device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, in
 }
 
 // Segment s's window covers columns [s segw - 16 TL, s segw - 16 TL + SW).
-__device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
-                                        const float* part_in, const float* b, int bb, const float* sdr) {
+__device__ __forceinline__ void window_segments(const Geom& g, int j, int& slo, int& shi) {
   const int segw = g.SB * kBlockRows;
   const int x = j + 16 * g.TL;
-  int shi = x / segw;
+  shi = x / segw;
   shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
-  int slo = floor_div(x - g.SW, segw) + 1;
+  slo = floor_div(x - g.SW, segw) + 1;
   slo = slo < 0 ? 0 : slo;
-  return gather_v_range(g, bh, n, j, slo, shi, v_prev2, part_in, b, bb, sdr);
+}
+
+template <bool COH = false>
+__device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
+                                        const float* part_in, const float* b, int bb, const float* sdr) {
+  int slo, shi;
+  window_segments(g, j, slo, shi);
+  return gather_v_range<COH>(g, bh, n, j, slo, shi, v_prev2, part_in, b, bb, sdr);
 }
 
 // v^(t-1)_j = v^(t-2)_j + log2(b_j / gamma_j), gamma_j = sum_i P^(t-1,t-2)_ij
@@ -185,6 +210,40 @@ __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, 
   return finish_from(gather_v(g, bh, n, j, v_prev2, part_in, b, bb, sdr), load_dust(g, bh, dstate));
 }
 
+// Steps t_begin .. t_end of one persistent launch (see iter_kernel): the
+// buffers each step reads and writes follow from t, as in the host's launch
+// loop.  progress[bh * nseg + seg] is the last step a segment has finished;
+// *err is set if a neighbour wait gave up (then the results are invalid).
+struct StepPlan {
+  float* part;       // [2][part_slot] column partials (by step parity)
+  double* vbuf;      // [2][BHL] v ping-pong
+  double* ubuf;      // [BHL] latest u
+  double* tail_u;    // [R + 1][BHL]
+  double* tail_v;    // [R + 1][BHL]
+  size_t part_slot, BHL;
+  int T;             // stopped-base steps
+  int t_begin, t_end;
+  int* progress;
+  int* err;
+};
+
+__device__ __forceinline__ IterArgs step_args(const IterArgs& base, const StepPlan& q, int t) {
+  IterArgs a = base;
+  a.first = t == 1;
+  a.part_in = t == 1 ? nullptr : q.part + (size_t)((t - 1) & 1) * q.part_slot;
+  a.v_prev2 = t <= 2 ? nullptr : q.vbuf + (size_t)((t - 2) & 1) * q.BHL;
+  a.v_out = t == 1 ? nullptr : q.vbuf + (size_t)((t - 1) & 1) * q.BHL;
+  a.v_tail = (t >= 2 && t - 1 >= q.T) ? q.tail_v + (size_t)(t - 1 - q.T) * q.BHL : nullptr;
+  a.u_out = q.ubuf;
+  a.u_tail = t >= q.T ? q.tail_u + (size_t)(t - q.T) * q.BHL : nullptr;
+  a.part_out = q.part + (size_t)(t & 1) * q.part_slot;
+  a.partd_out = nullptr;
+  a.dstate = nullptr;
+  return a;
+}
+
+constexpr int kMaxSpins = 1 << 20;  // bound of a neighbour wait (each spin sleeps ~256 cycles)
+
 // One launch = one Sinkhorn step over every (b, h).  A workgroup sweeps a
 // segment of SB consecutive 128-row blocks of one sequence:
 //  * the K window of a block (NWT tiles of 16 rows) lives in an LDS ring of
@@ -204,8 +263,15 @@ __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, 
 // NT (tiles per strip) and the ring size are compile-time; tiles that cross
 // the band edge (a host-computed bit mask) or strips with non-real rows are
 // masked per entry.
-template <typename T, int D, int NT>
-__global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
+//
+// PERS: one launch runs the steps of a StepPlan (no dustbin).  Sweeps
+// alternate direction, so the ring at the end of a step already holds the
+// window the next step starts with: between steps a workgroup only waits for
+// its two neighbouring segments to finish the step (their partials and v feed
+// its window columns) and finishes v for its window, instead of a new launch
+// reloading the window.  All workgroups must be resident (cooperative launch).
+template <typename T, int D, int NT, bool PERS>
+__global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan q) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
   constexpr int NCH = RB / 64;             // 16-byte lane chunks per row
   constexpr int RS = RB + 16;              // LDS row: K row + 16 bytes (conflict-free lane reads)
@@ -220,6 +286,68 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   constexpr int kThreads = 512;            // launch size (a constant: reading blockDim.x is a memory load)
   static_assert(kBlockRows * PER_ROW == NEWLD * kThreads, "whole 16-byte chunks per thread");
   extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const IterArgs& p = p0;  // step-independent arguments
+  const bool dust = !PERS && g.dustbin;  // (the persistent instance runs without a dustbin)
+  int t = PERS ? q.t_begin : 0;  // step (PERS)
+  // The step's buffers: from the arguments, or (PERS) from a copy in LDS
+  // that thread 0 derives from t at each step (LDS reads cannot move across
+  // the block barriers, so nothing per step stays live in registers across
+  // the sweep).
+  struct StepPtrs {
+    const float* part_in;
+    const double* v_prev2;
+    double* v_out;
+    double* v_tail;
+    double* u_tail;
+    float* part_out;
+    int first;
+  };
+  __shared__ StepPtrs sptr;
+  auto set_step = [&]() {
+    if (threadIdx.x == 0) {
+      const IterArgs a = step_args(p0, q, t);
+      sptr.part_in = a.part_in;
+      sptr.v_prev2 = a.v_prev2;
+      sptr.v_out = a.v_out;
+      sptr.v_tail = a.v_tail;
+      sptr.u_tail = a.u_tail;
+      sptr.part_out = a.part_out;
+      sptr.first = a.first;
+    }
+  };
+  auto s_part_in = [&]() -> const float* {
+    if constexpr (PERS) return sptr.part_in;
+    else return p0.part_in;
+  };
+  auto s_v_prev2 = [&]() -> const double* {
+    if constexpr (PERS) return sptr.v_prev2;
+    else return p0.v_prev2;
+  };
+  auto s_v_out = [&]() -> double* {
+    if constexpr (PERS) return sptr.v_out;
+    else return p0.v_out;
+  };
+  auto s_v_tail = [&]() -> double* {
+    if constexpr (PERS) return sptr.v_tail;
+    else return p0.v_tail;
+  };
+  auto s_u_out = [&]() -> double* {
+    if constexpr (PERS) return q.ubuf;
+    else return p0.u_out;
+  };
+  auto s_u_tail = [&]() -> double* {
+    if constexpr (PERS) return sptr.u_tail;
+    else return p0.u_tail;
+  };
+  auto s_part_out = [&]() -> float* {
+    if constexpr (PERS) return sptr.part_out;
+    else return p0.part_out;
+  };
+  auto s_first = [&]() -> bool {
+    if constexpr (PERS) return sptr.first != 0;
+    else return p0.first != 0;
+  };
 
   const int nbh = g.B * g.H;
   const int logical = xcd_remap(blockIdx.x, p.padded_grid);
@@ -256,16 +384,20 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
   const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
   const DustC dc = load_dust(g, bh, p.dstate);
-  const double vd = (g.dustbin && p.dstate) ? p.dstate[4 * bh + 1] : 0.0;  // v^(t-1)_delta
+  const double vd = (dust && p.dstate) ? p.dstate[4 * bh + 1] : 0.0;  // v^(t-1)_delta
 
   // shift reference: v^(t-2) at the segment's first column (any value near
   // the window's potentials keeps the entries in range)
-  const double vref = p.v_prev2 ? p.v_prev2[bh * L + seg_r0] : 0.0;
+  if constexpr (PERS) {
+    set_step();
+    __syncthreads();
+  }
+  double vref = s_v_prev2() ? ld_shared<PERS>(s_v_prev2() + bh * L + seg_r0) : 0.0;
 
   auto publish_v = [&](int j, double vj) {
-    if (p.v_out && j >= seg_r0 && j < seg_r1) {
-      p.v_out[bh * L + j] = vj;
-      if (p.v_tail) p.v_tail[bh * L + j] = vj;
+    if (s_v_out() && j >= seg_r0 && j < seg_r1) {
+      st_shared<PERS>(s_v_out() + bh * L + j, vj);
+      if (s_v_tail()) s_v_tail()[bh * L + j] = vj;
     }
   };
   auto wrap = [](int x) { return x >= RING ? x - RING : x; };  // x in [0, 2 RING)
@@ -291,11 +423,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     const int jc = jw + tid;
     const bool colok = tid < NWC && jc >= 0 && jc < n;
     VIn pin;
-    if (colok && p.part_in) pin = gather_v(g, bh, n, jc, p.v_prev2, p.part_in, p.b, bb, p.sdr);
+    if (colok && s_part_in()) pin = gather_v<PERS>(g, bh, n, jc, s_v_prev2(), s_part_in(), p.b, bb, p.sdr);
     if (tid < NWC) {
       float w = kNegInf;
       if (colok) {
-        const double vj = p.part_in ? finish_from(pin, dc) : 0.0;
+        const double vj = s_part_in() ? finish_from(pin, dc) : 0.0;
         publish_v(jc, vj);
         w = (float)(vj - vref);
       }
@@ -332,7 +464,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     for (int r = 0; r < 4; ++r) {
       const uint32_t i = (uint32_t)min(ib + r, (int)L - 1);
       ri.a[r] = a_b[i];
-      ri.sd[r] = sdc_bh[i];  // always allocated; used only with a dustbin
+      if constexpr (!PERS) ri.sd[r] = sdc_bh[i];  // always allocated; used only with a dustbin
     }
   };
   RowIn cur;
@@ -350,7 +482,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
   // (threads from kBlockRows on: the first two waves handle the entering
   // columns instead, which balances the work ahead of the block barrier)
   static_assert(NWC <= kThreads - kBlockRows, "one window column per folding thread");
-  auto fold = [&](int kf, int bf, int rbf, bool last) {
+  int dir = 1;  // sweep direction of the current step (always forward unless PERS)
+  auto fold = [&](int kf, int bf, int rbf, bool last, bool fwd) {
     const int wc = tid - kBlockRows;
     if (wc >= 0 && wc < NWC) {
       const int off = wc >> 4;                         // tile offset within block kf's window
@@ -366,14 +499,16 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         const float x = colbuf[(bf * kWaves + w) * CBW + lt * 16 + (wc & 15)];
         s += wrote ? x : 0.f;
       }
-      if (off < 8 || last) {
+      // columns leave at the low end of the window in a forward sweep, at
+      // the high end in a backward one
+      if ((fwd ? off < 8 : off >= NWT - 8) || last) {
         const int j = (kf * 8 - g.TL + off) * 16 + (wc & 15);
-        p.part_out[((size_t)bh * g.nseg + seg) * g.SW + (j - cs)] = s;
+        st_shared<PERS>(s_part_out() + ((size_t)bh * g.nseg + seg) * g.SW + (j - cs), s);
         s = 0.f;
       }
       colsum[c] = s;
     }
-    if (g.dustbin && tid == 0) {
+    if (dust && tid == 0) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
         if (kf * kBlockRows + 16 * w < n) dust_acc += misc[bf * kWaves + w];
@@ -389,20 +524,29 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     jpend = -1;
   };
   int rb = 0;                                   // ring slot of block k's first window tile
-  int rbp = 0;                                  // same for block k - 1
-  for (int k = b0; k < kend; ++k) {
-    const int buf = (k - b0) & 1;
-    const bool more = k + 1 < kend;
+  int rbp = 0;                                  // same for the previous block
+  const int nbs = kend - b0;                    // blocks in the segment
+  // One sweep over the segment's blocks (DIR = +1 forward, -1 backward: a
+  // compile-time direction, so each instantiation keeps one set of indices).
+  auto sweep = [&](auto dirc) {
+    constexpr int DIR = decltype(dirc)::value;
+  for (int bi = 0; bi < nbs; ++bi) {
+    const int k = DIR > 0 ? b0 + bi : kend - 1 - bi;
+    const int buf = bi & 1;
+    const bool more = bi + 1 < nbs;
     // ---- prefetch for block k + 1 (8 new K tiles, Q strips, a_i, column-
     // finish inputs) in NPF slices, one issued per tile of the strip's first
     // tiles: a wave issuing them all at once stalls on the CU's memory pipe.
     // The loads are unconditional (clamped addresses) so that no register
     // write on an untaken path makes the compiler wait for them early.
-    const int jn0 = ((k + 1) * 8 + g.TR) * 16;  // first new window row/column
-    // block whose inputs the slices load: k + 1, or k itself in the last block
-    // (nothing is used there; its rows are cached, so no extra HBM traffic)
-    const int kn = more ? k + 1 : k;
-    const int jp0 = (kn * 8 + g.TR) * 16;
+    // first row/column of the 8 tiles entering with the next block (the
+    // top of its window in a forward sweep, the bottom in a backward one)
+    const int jn0 = DIR > 0 ? ((k + 1) * 8 + g.TR) * 16 : ((k - 1) * 8 - g.TL) * 16;
+    // block whose inputs the slices load: the next one, or k itself in the
+    // last block (nothing is used there; its rows are cached, so no extra
+    // HBM traffic)
+    const int kn = more ? k + DIR : k;
+    const int jp0 = DIR > 0 ? (kn * 8 + g.TR) * 16 : (kn * 8 - g.TL) * 16;
     u4 knew[NEWLD];
     VIn vin;
     RowIn nxt;
@@ -413,30 +557,37 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       if (part < NEWLD) {
         // rows past the sequence are zeroed when stored to LDS
         // (a per-(b, h) base pointer plus a 32-bit lane offset: the load
-        // takes the scalar base directly, no 64-bit address arithmetic)
+        // takes the scalar base DIRectly, no 64-bit address arithmetic)
         const int idx = tid + part * kThreads;
-        const int j = min(jp0 + idx / PER_ROW, (int)L - 1);
+        int j = min(jp0 + idx / PER_ROW, (int)L - 1);
+        if constexpr (PERS) j = max(j, 0);
         knew[part] = ld16(Kb + (uint32_t)(j * RB + (idx % PER_ROW) * 16));
       } else if (part < NEWLD + NCH) {
         load_q_chunk(kn, part - NEWLD, nxt);
       } else if (part == NEWLD + NCH) {
         load_row_scalars(kn, nxt);
-      } else if (ec >= 0 && p.part_in) {
+      } else if (ec >= 0 && s_part_in()) {
         // j + 16 TL = (k + 1) 128 + 16 (TL + TR) + ec with ec < 128, so the
         // first segment window holding j is (k + 1) / SB and the last is at
         // most two further (16 (TL + TR) <= 256 <= 2 segw)
         int j = jp0 + ec;
-        const int segw = g.SB * kBlockRows;
-        const int slo = kn / g.SB;
-        const int x = j + 16 * g.TL;
-        int shi = slo + (x >= (slo + 1) * segw ? 1 : 0) + (x >= (slo + 2) * segw ? 1 : 0);
-        shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
-        j = j < (int)L ? j : (int)L - 1;  // columns past the sequence are not used
-        vin = gather_v_clamped(g, bh, n, j, slo, shi, p.v_prev2, p.part_in, p.b, bb, p.sdr);
+        int slo, shi;
+        if constexpr (PERS) {
+          window_segments(g, j, slo, shi);
+          j = j < 0 ? 0 : j;
+        } else {
+          const int segw = g.SB * kBlockRows;
+          slo = kn / g.SB;
+          const int x = j + 16 * g.TL;
+          shi = slo + (x >= (slo + 1) * segw ? 1 : 0) + (x >= (slo + 2) * segw ? 1 : 0);
+          shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
+        }
+        j = j < (int)L ? j : (int)L - 1;  // columns outside the sequence are not used
+        vin = gather_v_clamped<PERS>(g, bh, n, j, slo, shi, s_v_prev2(), s_part_in(), p.b, bb, p.sdr);
       }
     };
-    // ---- partials of block k - 1 into the segment sums
-    if (k > b0) fold(k - 1, buf ^ 1, rbp, false);
+    // ---- partials of the previous block into the segment sums
+    if (bi > 0) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0);
 
     // ---- block k: one 16-row strip per wave (all strip values wave-uniform)
     const int i0 = k * kBlockRows + wave * 16;
@@ -453,7 +604,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       for (int r = 0; r < 4; ++r) rowok[r] = i0 + 4 * lg + r < n;
       // dustbin column exponent for the lane's rows, relative to vref
       float xd[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-      if (g.dustbin) {
+      if (dust) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (rowok[r]) xd[r] = (float)((double)cur.sd[r] + vd - vref);
@@ -497,7 +648,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
       // the exact row maxima below (and issues the prefetch slices itself);
       // when a fast row sum leaves the safe range the strip is recomputed
       // there as well.
-      bool need_safe = p.first != 0;
+      bool need_safe = s_first() != 0;
       if (!need_safe) {
         // fast path: shift vref only; pipelined MFMA / exp
         auto consume = [&](int t, const f4& acc, float w) {
@@ -550,7 +701,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           rs[r] = row16_sum(rs[r]);
-          if (g.dustbin) {
+          if (dust) {
             ed[r] = exp2_fast(xd[r]);
             rs[r] += ed[r];
           }
@@ -579,7 +730,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           m[r] = row16_max(m[r]);
-          if (g.dustbin) m[r] = fmaxf(m[r], xd[r]);
+          if (dust) m[r] = fmaxf(m[r], xd[r]);
           if (!(m[r] > kNegInf)) m[r] = 0.f;  // inactive row
           shift[r] = m[r];
           rs[r] = 0.f;
@@ -595,7 +746,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           rs[r] = row16_sum(rs[r]);
-          ed[r] = g.dustbin ? exp2_fast(xd[r] - shift[r]) : 0.f;
+          ed[r] = dust ? exp2_fast(xd[r] - shift[r]) : 0.f;
           rs[r] += ed[r];
         }
       }
@@ -620,8 +771,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         if (lr < 4 && okv) {
           const int i = i0 + 4 * lg + rsel;
           const double u = (double)log2f(av / rsv) - (double)shv - vref;
-          p.u_out[bh * L + i] = u;
-          if (p.u_tail) p.u_tail[bh * L + i] = u;
+          s_u_out()[bh * L + i] = u;
+          if (s_u_tail()) s_u_tail()[bh * L + i] = u;
         }
       }
       // column partials of this strip, sum_i e_ij h_i, reduced over the four
@@ -643,7 +794,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         const float s1 = cross_row_sum(colp(t));
         if (lg == 0) cb[t * 16 + lr] = s1;
       }
-      if (g.dustbin) {
+      if (dust) {
         float dp = 0.f;
         if (lr == 0) {
 #pragma unroll
@@ -663,7 +814,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     if (more && ec >= 0) {
       const int j = jn0 + ec;
       if (j >= 0 && j < n) {
-        const double vj = p.part_in ? finish_from(vin, dc) : 0.0;
+        const double vj = s_part_in() ? finish_from(vin, dc) : 0.0;
         jpend = j;
         vpend = vj;
         wnew = (float)(vj - vref);
@@ -679,7 +830,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
         const int idx = tid + e * 512;
         const int row = idx / PER_ROW;
         const int j = jn0 + row;
-        const u4 val = j < n ? knew[e] : (u4){0u, 0u, 0u, 0u};
+        const bool jok = PERS ? (j >= 0 && j < n) : j < n;
+        const u4 val = jok ? knew[e] : (u4){0u, 0u, 0u, 0u};
         st16(kw + (size_t)(wrap(rb + NWT + (row >> 4)) * 16 + (row & 15)) * RS + (idx % PER_ROW) * 16, val);
       }
       if (ec >= 0) put_w(wrap(rb + NWT + (ec >> 4)) * 16 + (ec & 15), wnew);
@@ -688,13 +840,71 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p) {
     if (more) {
       cur = nxt;
       rbp = rb;
-      rb = wrap(rb + 8);
+      rb = wrap(rb + (DIR > 0 ? 8 : NWT));  // NWT = -8 modulo the ring
     }
   }
-  flush_pending();
-  // the last block's partials; every column still in the window leaves
-  fold(kend - 1, (kend - 1 - b0) & 1, rb, true);
-  if (g.dustbin && tid == 0) p.partd_out[(size_t)bh * g.nseg + seg] = dust_acc;
+    flush_pending();
+    // the last block's partials; every column still in the window leaves
+    fold(DIR > 0 ? kend - 1 : b0, (nbs - 1) & 1, rb, true, DIR > 0);
+  };
+  for (;;) {
+  if constexpr (PERS) {
+    if (dir > 0) sweep(std::integral_constant<int, 1>{});
+    else sweep(std::integral_constant<int, -1>{});
+  } else {
+    sweep(std::integral_constant<int, 1>{});
+  }
+  if constexpr (!PERS) {
+    break;
+  } else {
+    if (t == q.t_end) break;
+    // ---- next step: publish this segment's progress (every store of step t
+    // is complete), wait for the neighbouring segments, then finish v^(t) for
+    // the window the new sweep starts with (its K rows are in the ring)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int me = bh * g.nseg + seg;
+      st_shared<true>(q.progress + me, t);
+      const bool has_l = seg > 0;
+      const bool has_r = seg + 1 < g.nseg && (seg + 1) * g.SB * kBlockRows < n;
+      int spins = 0;
+      while ((has_l && ld_shared<true>(q.progress + me - 1) < t) ||
+             (has_r && ld_shared<true>(q.progress + me + 1) < t)) {
+        if (++spins > kMaxSpins) {
+          st_shared<true>(q.err, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    __syncthreads();
+    ++t;
+    dir = -dir;
+    set_step();
+    __syncthreads();
+    vref = s_v_prev2() ? ld_shared<true>(s_v_prev2() + bh * L + seg_r0) : 0.0;
+    {
+      const int kc = dir > 0 ? b0 : kend - 1;  // the block the new sweep starts at
+      const int jc = (kc * 8 - g.TL) * 16 + tid;
+      const bool colok = tid < NWC && jc >= 0 && jc < n;
+      VIn pin;
+      if (colok && s_part_in()) pin = gather_v<true>(g, bh, n, jc, s_v_prev2(), s_part_in(), p.b, bb, p.sdr);
+      if (tid < NWC) {
+        float w = kNegInf;
+        if (colok) {
+          const double vj = s_part_in() ? finish_from(pin, dc) : 0.0;
+          publish_v(jc, vj);
+          w = (float)(vj - vref);
+        }
+        put_w(wrap(rb + (tid >> 4)) * 16 + (tid & 15), w);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+  }
+  if (dust && tid == 0) p.partd_out[(size_t)bh * g.nseg + seg] = dust_acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -1329,6 +1539,20 @@ __global__ __launch_bounds__(256) void dustbin_output(Geom g, const T* V, const 
   }
 }
 
+__global__ void fill_int(int* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// A neighbour wait of the persistent step kernel gave up (results invalid):
+// make that visible in the outputs.
+__global__ void step_wait_failed(const int* err, float* O, float* u) {
+  if (*err) {
+    O[0] = __builtin_nanf("");
+    u[0] = __builtin_nanf("");
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host launcher for the whole forward pass.
 // ---------------------------------------------------------------------------
@@ -1349,11 +1573,23 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   if (iter_lds > 160 * 1024 || out_lds > 160 * 1024) return hipErrorInvalidConfiguration;
   // compile-time tile count: the smallest instance covering the band
   const void* ik;
-  if (g.NT <= 3) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 3>);
-  else if (g.NT <= 5) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 5>);
-  else if (g.NT <= 9) ik = reinterpret_cast<const void*>(iter_kernel<T, D, 9>);
-  else ik = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles>);
+  const void* ikp;  // persistent instance
+  if (g.NT <= 3) {
+    ik = reinterpret_cast<const void*>(iter_kernel<T, D, 3, false>);
+    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, 3, true>);
+  } else if (g.NT <= 5) {
+    ik = reinterpret_cast<const void*>(iter_kernel<T, D, 5, false>);
+    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, 5, true>);
+  } else if (g.NT <= 9) {
+    ik = reinterpret_cast<const void*>(iter_kernel<T, D, 9, false>);
+    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, 9, true>);
+  } else {
+    ik = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles, false>);
+    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles, true>);
+  }
   err = hipFuncSetAttribute(ik, hipFuncAttributeMaxDynamicSharedMemorySize, (int)iter_lds);
+  if (err != hipSuccess) return err;
+  err = hipFuncSetAttribute(ikp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)iter_lds);
   if (err != hipSuccess) return err;
   err = hipFuncSetAttribute(reinterpret_cast<const void*>(output_kernel<T, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
@@ -1405,13 +1641,17 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     const bool tm = timing_enabled() && !stop_early;
     if (tm && (g.dustbin || t == 1)) timing_mark(st, false);
     if (g.NT <= 3)
-      hipLaunchKernelGGL((iter_kernel<T, D, 3>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+      hipLaunchKernelGGL((iter_kernel<T, D, 3, false>), dim3(iter_grid), dim3(512), iter_lds, st, g, a,
+                         StepPlan{});
     else if (g.NT <= 5)
-      hipLaunchKernelGGL((iter_kernel<T, D, 5>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+      hipLaunchKernelGGL((iter_kernel<T, D, 5, false>), dim3(iter_grid), dim3(512), iter_lds, st, g, a,
+                         StepPlan{});
     else if (g.NT <= 9)
-      hipLaunchKernelGGL((iter_kernel<T, D, 9>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+      hipLaunchKernelGGL((iter_kernel<T, D, 9, false>), dim3(iter_grid), dim3(512), iter_lds, st, g, a,
+                         StepPlan{});
     else
-      hipLaunchKernelGGL((iter_kernel<T, D, kMaxTiles>), dim3(iter_grid), dim3(512), iter_lds, st, g, a);
+      hipLaunchKernelGGL((iter_kernel<T, D, kMaxTiles, false>), dim3(iter_grid), dim3(512), iter_lds, st, g, a,
+                         StepPlan{});
     if (tm && (g.dustbin || t == N)) timing_mark(st, true, g.dustbin ? 1 : N);
     if (g.dustbin) {
       DustArgs da{};
@@ -1438,7 +1678,43 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   // e_c < tol; step c + 1 is then the first tail step.
   int Tb = f.T;
   int t = 1;
-  if (stop_early) {
+  const int N = f.T + f.R;
+  // Every step in one cooperative launch of the persistent instance, when all
+  // its workgroups fit on the device at once (no dustbin, no early stop; set
+  // SINKATTN_STEP_LAUNCHES to launch once per step instead).
+  bool persistent = false;
+  if (N >= 2 && !g.dustbin && !stop_early && !std::getenv("SINKATTN_STEP_LAUNCHES")) {
+    int dev = 0, coop = 0, cus = 0, per = 0;
+    err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, ikp, 512, iter_lds);
+    if (err != hipSuccess) return err;
+    if (coop && (long long)per * cus >= iter_grid) {
+      const int nprog = nbh * g.nseg + 1;
+      hipLaunchKernelGGL(fill_int, dim3((nprog + 255) / 256), dim3(256), 0, st, w.prog, nprog, 0);
+      IterArgs a{};
+      a.Q = f.Q;
+      a.K = f.K;
+      a.a = f.a;
+      a.b = f.b;
+      a.sdr = w.sdr;
+      a.sdc = w.sdc;
+      a.padded_grid = iter_grid;
+      StepPlan q{w.part, w.vbuf, w.ubuf, w.tail_u, w.tail_v, part_slot, BHL, f.T, 1, N, w.prog,
+                 w.prog + nbh * g.nseg};
+      Geom gg = g;
+      void* args[] = {&gg, &a, &q};
+      if (timing_enabled()) timing_mark(st, false);
+      err = hipLaunchCooperativeKernel(ikp, dim3(iter_grid), dim3(512), args, (unsigned)iter_lds, st);
+      if (err != hipSuccess) return err;
+      if (timing_enabled()) timing_mark(st, true, N);
+      persistent = true;
+      t = N + 1;
+    }
+  }
+  if (persistent) {
+  } else if (stop_early) {
     std::vector<double> eh((size_t)nbh);
     for (; t <= f.T; ++t) {
       const int c = t - 1;
@@ -1468,17 +1744,17 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   }
   for (; t <= Tb + f.R; ++t) launch_step(t, Tb, false);
   if (f.stop.T_used) *f.stop.T_used = Tb;
-  const int N = Tb + f.R;
+  const int Nrun = Tb + f.R;
   OutArgs o{};
   o.Q = f.Q;
   o.K = f.K;
   o.V = f.V;
   o.a = f.a;
   o.b = f.b;
-  o.part_in = (N == 0) ? nullptr : w.part + (size_t)(N & 1) * part_slot;
-  o.v_prev2 = (N <= 1) ? nullptr : w.vbuf + (size_t)((N - 1) & 1) * BHL;
-  o.u_in = (N == 0) ? nullptr : w.ubuf;
-  o.dstate = (g.dustbin && N >= 1) ? w.dstate : nullptr;
+  o.part_in = (Nrun == 0) ? nullptr : w.part + (size_t)(Nrun & 1) * part_slot;
+  o.v_prev2 = (Nrun <= 1) ? nullptr : w.vbuf + (size_t)((Nrun - 1) & 1) * BHL;
+  o.u_in = (Nrun == 0) ? nullptr : w.ubuf;
+  o.dstate = (g.dustbin && Nrun >= 1) ? w.dstate : nullptr;
   o.sdr = w.sdr;
   o.sdc = w.sdc;
   o.O = f.O;
@@ -1496,6 +1772,8 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   } else {
     hipLaunchKernelGGL((output_kernel<T, D>), dim3(grid), dim3(512), out_lds, st, g, o);
   }
+  if (persistent)
+    hipLaunchKernelGGL(step_wait_failed, dim3(1), dim3(1), 0, st, w.prog + nbh * g.nseg, f.O, f.u);
   if (g.dustbin) {
     hipLaunchKernelGGL(dustbin_output<T>, dim3(nbh), dim3(128), 0, st, g, reinterpret_cast<const T*>(f.V),
                        w.tail_v + (size_t)f.R * BHL, o.dstate, w.sdr, f.O, f.u, f.v);
