@@ -125,9 +125,10 @@ def step_geometry(B, H, L, W):
 
 
 def load_pmc(launch_units=None):
-    """HBM traffic per launch of the fused step from committed rocprofv3
-    counters, scaled by a copy-kernel calibration; None if absent or taken
-    on different kernel sources."""
+    """HBM traffic per Sinkhorn step of the fused step kernel from committed
+    rocprofv3 counters (per dispatch / steps per dispatch), scaled by a
+    copy-kernel calibration; None if absent or taken on different kernel
+    sources."""
     try:
         with open(PMC_FILE) as f:
             pmc = json.load(f)
@@ -135,17 +136,24 @@ def load_pmc(launch_units=None):
         return None
     if pmc.get("kernel_source_hash") != kernel_source_hash():
         return None
-    fetch = pmc["fetch_kib_per_dispatch"] * pmc["fetch_scale"]
-    write = pmc["write_kib_per_dispatch"] * pmc["write_scale"]
+    fetch = pmc["fetch_kib_per_step"] * pmc["fetch_scale"]
+    write = pmc["write_kib_per_step"] * pmc["write_scale"]
     return (fetch + write) * 1024.0
 
 
+PROF_ARGS = "--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0"
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $REPO/gpurun_out/prof/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
-             "--no-cpu-baseline")
+             + PROF_ARGS)
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
            "-d $REPO/gpurun_out/prof/{sub} -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 "
-           "--no-cpu-baseline --copy-calibration")
+           + PROF_ARGS + " --copy-calibration")
+
+
+def steps_per_dispatch(name):
+    """Sinkhorn steps one dispatch of the fused step kernel covers: all T + R
+    of a forward for the persistent instance (template flag true), else 1."""
+    return CONFIG["T"] + CONFIG["R"] if ", true>" in name else 1
 
 
 def _csv_rows(path):
@@ -170,9 +178,11 @@ def summarize(d):
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
     it = [r for r in stats if "iter_kernel" in r["Name"]]
     if it:
-        lines += ["", f"fused step (iter_kernel): {int(it[0]['Calls'])} dispatches, average "
-                  f"{float(it[0]['AverageNs']) / 1e3:.2f} us, min {float(it[0]['MinNs']) / 1e3:.2f} us, "
-                  f"max {float(it[0]['MaxNs']) / 1e3:.2f} us"]
+        spd = steps_per_dispatch(it[0]["Name"])
+        lines += ["", f"fused step (iter_kernel): {int(it[0]['Calls'])} dispatches of {spd} step(s), average "
+                  f"{float(it[0]['AverageNs']) / 1e3:.2f} us per dispatch = "
+                  f"{float(it[0]['AverageNs']) / 1e3 / spd:.2f} us per step "
+                  f"(min {float(it[0]['MinNs']) / 1e3 / spd:.2f}, max {float(it[0]['MaxNs']) / 1e3 / spd:.2f})"]
     logf = os.path.join(d, "trace.log")
     if os.path.exists(logf):
         for ln in open(logf):
@@ -184,28 +194,31 @@ def summarize(d):
         if not files:
             continue
         rows = [r for r in _csv_rows(files[0]) if r["Counter_Name"] == ctr]
-        itv = [float(r["Counter_Value"]) for r in rows if "iter_kernel" in r["Kernel_Name"]]
+        itr = [r for r in rows if "iter_kernel" in r["Kernel_Name"]]
+        itv = [float(r["Counter_Value"]) / steps_per_dispatch(r["Kernel_Name"]) for r in itr]
         cp = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
         if not itv or not cp:
             continue
         copy_kib = max(cp)  # the 256 MiB calibration copy is the largest copy dispatch
-        pmc[f"{key}_kib_per_dispatch"] = sum(itv) / len(itv)
+        pmc[f"{key}_kib_per_step"] = sum(itv) / len(itv)
         pmc[f"{key}_dispatches"] = len(itv)
+        pmc[f"{key}_steps_per_dispatch"] = steps_per_dispatch(itr[0]["Kernel_Name"])
         pmc[f"{key}_copy_kib"] = copy_kib
         pmc[f"{key}_scale"] = (COPY_BYTES / 1024.0) / copy_kib
         pmc[f"{key}_command"] = PMC_CMD.format(ctr=ctr, sub=sub)
     if "fetch_scale" in pmc and "write_scale" in pmc:
-        fetch = pmc["fetch_kib_per_dispatch"] * pmc["fetch_scale"] * 1024
-        write = pmc["write_kib_per_dispatch"] * pmc["write_scale"] * 1024
+        fetch = pmc["fetch_kib_per_step"] * pmc["fetch_scale"] * 1024
+        write = pmc["write_kib_per_step"] * pmc["write_scale"] * 1024
         SB, TL, TR = step_geometry(1, 8, 32768, 256)
         alg = step_bytes_per_launch(1, 8, 32768, 128, 2, SB, TL, TR)
         lines += ["", "HBM traffic of the fused step (rocprofv3 --pmc, one counter per run):",
                   "  " + pmc["fetch_command"], "  " + pmc["write_command"],
-                  f"  FETCH_SIZE {pmc['fetch_kib_per_dispatch']:.0f} KiB/dispatch x {pmc['fetch_scale']:.3f} "
+                  f"  FETCH_SIZE {pmc['fetch_kib_per_step']:.0f} KiB/step "
+                  f"({pmc['fetch_steps_per_dispatch']} steps per dispatch) x {pmc['fetch_scale']:.3f} "
                   f"(256 MiB copy read {pmc['fetch_copy_kib']:.0f} KiB) = {fetch / 1e6:.1f} MB",
-                  f"  WRITE_SIZE {pmc['write_kib_per_dispatch']:.0f} KiB/dispatch x {pmc['write_scale']:.3f} "
+                  f"  WRITE_SIZE {pmc['write_kib_per_step']:.0f} KiB/step x {pmc['write_scale']:.3f} "
                   f"(256 MiB copy wrote {pmc['write_copy_kib']:.0f} KiB) = {write / 1e6:.1f} MB",
-                  f"  total {(fetch + write) / 1e6:.1f} MB per launch; algorithmic {alg / 1e6:.1f} MB "
+                  f"  total {(fetch + write) / 1e6:.1f} MB per step; algorithmic {alg / 1e6:.1f} MB "
                   f"(ratio {(fetch + write) / alg:.3f})",
                   f"  kernel sources hash {pmc['kernel_source_hash']}"]
         with open(PMC_FILE, "w") as f:
@@ -401,24 +414,26 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
     omega, ex_flops, ex_exps, sv_flops, sv_exps = work_counts(prob.B, prob.H, prob.L, prob.d, W, T, R)
     peak = PEAK_MFMA[prob.dtype]
-    # Dominant kernel: the fused Sinkhorn step (T + R launches per forward).
-    # Its tightest roofline is HBM: each launch streams every Q and K row.
-    avg_launch_s = (iter_ms / iter_launches) * 1e-3 if iter_launches else float("nan")
+    # Dominant kernel: the fused Sinkhorn step (T + R steps per forward, all in
+    # one persistent launch).  Its tightest roofline is HBM: each step streams
+    # every Q and K row.  Timed with HIP events around the step launch(es);
+    # figures are per Sinkhorn step.
+    avg_step_s = (iter_ms / iter_launches) * 1e-3 if iter_launches else float("nan")
     esize = 2 if prob.dtype == "bf16" else 4
     SB, TL, TR = step_geometry(prob.B, prob.H, prob.L, W)
-    launch_bytes = step_bytes_per_launch(prob.B, prob.H, prob.L, prob.d, esize, SB, TL, TR)
-    launch_flops = omega * 2 * prob.d
-    achieved = launch_bytes / avg_launch_s
+    step_bytes = step_bytes_per_launch(prob.B, prob.H, prob.L, prob.d, esize, SB, TL, TR)
+    step_flops = omega * 2 * prob.d
+    achieved = step_bytes / avg_step_s
     traffic = load_pmc()
     roofline = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
                 "traffic": None if traffic is None else round(traffic / 1e9, 4),
-                "kernel": "iter_kernel (fused Sinkhorn step)",
-                "avg_launch_us": round(avg_launch_s * 1e6, 3), "launches": iter_launches,
-                "bytes_per_launch": int(launch_bytes),
-                "traffic_unit": "GB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "mfma_frac": round(launch_flops / avg_launch_s / peak, 4),
-                "exp_frac": round(omega / avg_launch_s / PEAK_EXP, 4)}
+                "kernel": "iter_kernel (fused Sinkhorn step; persistent: T + R steps per launch)",
+                "avg_step_us": round(avg_step_s * 1e6, 3), "steps_timed": iter_launches,
+                "bytes_per_step": int(step_bytes),
+                "traffic_unit": "GB per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "mfma_frac": round(step_flops / avg_step_s / peak, 4),
+                "exp_frac": round(omega / avg_step_s / PEAK_EXP, 4)}
     t_s = ms_per_step * 1e-3
     path = {"executed": {"flops": ex_flops, "exps": ex_exps,
                          "frac": round(max(ex_flops / peak, ex_exps / PEAK_EXP) / t_s, 4)},

@@ -214,16 +214,18 @@ int sinkattn_block_contraction(const void *Q, const void *K, int W, const sinkat
 
 /* Diagnostics for benchmarking: timing of the fused Sinkhorn step kernel,
  * which dominates the run time.  While enabled (on != 0), sinkattn_forward
- * records HIP events on the caller's stream around its step-kernel launches:
- * one pair around the whole back-to-back run of T + R launches, or (with a
- * dustbin, whose own kernel runs between steps) one pair per launch.
- * sinkattn_timing_collect waits for the recorded events, writes the summed
- * bracketed time in milliseconds and the number of step-kernel launches it
- * covers since the previous collect (or enable), and resets the counters.  Process-wide state, not thread-safe; events are created
+ * records HIP events on the caller's stream around its step-kernel work: one
+ * pair around the single persistent launch that runs all T + R steps, or
+ * around the back-to-back run of T + R per-step launches, or (with a dustbin,
+ * whose own kernel runs between steps) one pair per launch; sinkattn_forward_
+ * converge records none.  sinkattn_timing_collect waits for the recorded
+ * events, writes the summed bracketed time in milliseconds and the number of
+ * Sinkhorn steps it covers since the previous collect (or enable), and resets
+ * the counters.  Process-wide state, not thread-safe; events are created
  * lazily and reused.  Returns SINKATTN_OK, SINKATTN_EINVAL (NULL outputs) or
  * SINKATTN_EHIP. */
 int sinkattn_timing_enable(int on);
-int sinkattn_timing_collect(double *total_ms, long long *launches);
+int sinkattn_timing_collect(double *total_ms, long long *steps);
 
 /* Human-readable text for a status code (static storage). */
 const char *sinkattn_status_string(int status);
