@@ -54,6 +54,8 @@ struct BwArgs {
   float* vbar;          // [R+1][BHL]
   float* x;             // [R+1][BHL]
   float* out;           // dQ / dK / dV
+  float* e_out;         // dV sweep, no dustbin: E_j = V_j . dV_j written here (vbar^(R)), and
+                        // filler rows of dV zeroed, in the sweep itself (nullptr: a later pass)
   int R;
   int r;                // pass index (vector sweeps)
   int padded_grid;
@@ -812,7 +814,22 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   const int bb = bh / g.H;
   const int n = real_len(g, bb);
   const int s0b = blk * 128;
-  if (s0b >= n) return;
+  // dV with E fused: rows [s0b, s0b + 128) of dV and of E are written by this
+  // workgroup even where they are filler (zeros)
+  auto zero_rows = [&](int s_lo) {
+    for (int e = threadIdx.x; e < 128 * D; e += kSwThreads) {
+      const int s = s0b + e / D;
+      if (s >= s_lo && s < g.L) p.out[((size_t)bh * g.L + s) * D + e % D] = 0.f;
+    }
+    for (int e = threadIdx.x; e < 128; e += kSwThreads) {
+      const int s = s0b + e;
+      if (s >= s_lo && s < g.L) p.e_out[(size_t)bh * g.L + s] = 0.f;
+    }
+  };
+  if (s0b >= n) {
+    if (MODE == 2 && p.e_out) zero_rows(s0b);
+    return;
+  }
   const size_t L = g.L;
   const size_t BHL = (size_t)nbh * L;
   const int R = p.R;
@@ -1055,7 +1072,24 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
     __syncthreads();
   }
 
-  if (!wactive) return;
+  if (!wactive) {
+    if (MODE == 2 && p.e_out) {  // filler strip: zero dV rows and E
+#pragma unroll
+      for (int ds = 0; ds < ND; ++ds)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = sidx0 + 4 * lg + r;
+          if (s < (int)L) p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = 0.f;
+        }
+      if (lr == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = sidx0 + 4 * lg + r;
+          if (s < (int)L) p.e_out[(size_t)bh * L + s] = 0.f;
+        }
+    }
+    return;
+  }
   if (MODE == 0) {
     const float tot = cross_row_sum(vacc);
     if (lg == 0 && sok) {
@@ -1087,13 +1121,32 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
     }
   } else {
     const float sc = MODE == 1 ? g.inv_sqrt_d : 1.f;
+    const bool fuse_e = MODE == 2 && p.e_out != nullptr;
+    float e4[4] = {0.f, 0.f, 0.f, 0.f};  // E partials of the lane's four columns
+    const unsigned short* Vb = reinterpret_cast<const unsigned short*>(p.V);
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = sidx0 + 4 * lg + r;
-        if (s < n) p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = acc[ds][r] * sc;
+        if (s < n) {
+          p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = acc[ds][r] * sc;
+          if (fuse_e) e4[r] = __builtin_fmaf(bf16_to_float(Vb[((size_t)bh * L + s) * D + ds * 16 + lr]), acc[ds][r], e4[r]);
+        } else if (fuse_e && s < (int)L) {
+          p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = 0.f;
+        }
       }
+    }
+    if (fuse_e) {
+      // E_j = sum over d of V_jd dV_jd: the lane's 8 slices, then its 16-lane row
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e4[r] = row16_sum(e4[r]);
+      if (lr == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = sidx0 + 4 * lg + r;
+          if (s < (int)L) p.e_out[(size_t)bh * L + s] = s < n ? e4[r] : 0.f;
+        }
     }
   }
 }
@@ -1178,15 +1231,20 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     SET_SW(false, 1, kMaxR) SET_SW(true, 1, kMaxR)
 #undef SET_SW
   }
-  // dV (band) -> add dustbin row, E, vbar^(R)
+  // dV (band) -> add dustbin row, E, vbar^(R).  The bf16 sweep computes E and
+  // zeroes filler rows itself when there is no dustbin term to add first.
   p.out = f.dV;
   ps.out = f.dV;
+  const bool fuse_e = kSweep && !g.dustbin;
+  ps.e_out = fuse_e ? vbar + (size_t)R * BHL : nullptr;
   if constexpr (kSweep)
     hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
   else
     hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
-  hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, tail_u, tail_v, w.sdr, R, f.dV,
-                     vbar + (size_t)R * BHL);
+  if (!fuse_e)
+    hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, tail_u, tail_v, w.sdr, R, f.dV,
+                       vbar + (size_t)R * BHL);
+  ps.e_out = nullptr;  // the later sweeps write no E
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
   // adjoint vectors through the tail
   for (int r = R; r >= 1; --r) {
