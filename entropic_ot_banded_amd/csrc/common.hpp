@@ -26,6 +26,10 @@ typedef uint16_t bf16_t;  // storage type of bf16 tensors
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// s_waitcnt immediate that waits for every vector memory operation of the
+// wave (vmcnt = 0) and leaves the LDS/scalar and export counters free
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }

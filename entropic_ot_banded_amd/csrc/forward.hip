@@ -256,10 +256,12 @@ constexpr int kMaxSpins = 1 << 20;  // bound of a neighbour wait (each spin slee
 //    off the barrier-to-barrier path; a column's sum is written once, when
 //    the column leaves the window;
 //  * the next block's K rows, Q strips, a_i and column-finish inputs are
-//    loaded into registers while the current block computes (the strip issues
-//    no global loads, so those loads stay in flight), and its 8 new K tiles go
-//    to the ring's 8 spare slots as soon as a wave's strip is done, so one
-//    barrier per block suffices.
+//    loaded while the current block computes (the strip issues no other
+//    global loads, so those loads stay in flight); its 8 new K tiles go to
+//    the ring's 8 spare slots, which no strip of the current block reads, so
+//    one barrier per block suffices.  256-byte rows are copied by LDS DMA
+//    straight into their ring rows (no registers, no store phase); other row
+//    sizes pass through registers and are stored when a wave's strip is done.
 // NT (tiles per strip) and the ring size are compile-time; tiles that cross
 // the band edge (a host-computed bit mask) or strips with non-real rows are
 // masked per entry.
@@ -278,6 +280,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   constexpr int TILEB = 16 * RS;           // bytes per ring tile
   constexpr int PER_ROW = RB / 16;         // 16-byte chunks per row
   constexpr int NEWLD = (kBlockRows * PER_ROW + 511) / 512;  // chunks per thread per block
+  // 256-byte rows: the next block's K rows go straight from memory into
+  // their ring rows (LDS DMA, one row per instruction, a dword per lane)
+  constexpr bool KDMA = RB == 256;
   constexpr int NWT = NT + kWaves - 1;     // window tiles of one block
   constexpr int NWC = NWT * 16;
   constexpr int RING = NWT + 8;            // ring tiles: the window + the next block's 8 new tiles
@@ -547,7 +552,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     // HBM traffic)
     const int kn = more ? k + DIR : k;
     const int jp0 = DIR > 0 ? (kn * 8 + g.TR) * 16 : (kn * 8 - g.TL) * 16;
-    u4 knew[NEWLD];
+    u4 knew[KDMA ? 1 : NEWLD];
     VIn vin;
     RowIn nxt;
     constexpr int NPF = NEWLD + NCH + 2;
@@ -555,13 +560,32 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     // every address is clamped into its buffer)
     auto prefetch = [&](int part) {
       if (part < NEWLD) {
-        // rows past the sequence are zeroed when stored to LDS
-        // (a per-(b, h) base pointer plus a 32-bit lane offset: the load
-        // takes the scalar base DIRectly, no 64-bit address arithmetic)
-        const int idx = tid + part * kThreads;
-        int j = min(jp0 + idx / PER_ROW, (int)L - 1);
-        if constexpr (PERS) j = max(j, 0);
-        knew[part] = ld16(Kb + (uint32_t)(j * RB + (idx % PER_ROW) * 16));
+        if constexpr (KDMA) {
+          // wave w fills new tile w (ring slot rb + NWT + w), 16 / NEWLD rows
+          // per slice.  Rows outside the sequence are loaded from the
+          // nearest real row: their columns carry w = -inf, so every entry
+          // they feed is exactly zero.  Nothing is loaded in the segment's
+          // last block (a DMA still in flight when the workgroup ends could
+          // land in another workgroup's LDS).
+          if (more) {
+            const int slot = wrap(rb + NWT + wave);
+#pragma unroll
+            for (int i = 0; i < 16 / NEWLD; ++i) {
+              const int r = (16 / NEWLD) * part + i;
+              int j = jp0 + wave * 16 + r;
+              j = j < 0 ? 0 : (j >= n ? n - 1 : j);
+              __builtin_amdgcn_global_load_lds(Kb + (uint32_t)(j * RB + lane * 4), kw + (slot * 16 + r) * RS, 4, 0, 0);
+            }
+          }
+        } else {
+          // rows past the sequence are zeroed when stored to LDS
+          // (a per-(b, h) base pointer plus a 32-bit lane offset: the load
+          // takes the scalar base DIRectly, no 64-bit address arithmetic)
+          const int idx = tid + part * kThreads;
+          int j = min(jp0 + idx / PER_ROW, (int)L - 1);
+          if constexpr (PERS) j = max(j, 0);
+          knew[part] = ld16(Kb + (uint32_t)(j * RB + (idx % PER_ROW) * 16));
+        }
       } else if (part < NEWLD + NCH) {
         load_q_chunk(kn, part - NEWLD, nxt);
       } else if (part == NEWLD + NCH) {
@@ -751,6 +775,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         }
       }
 
+      // the DMA rows of the next block are complete before this wave's
+      // stores below (waiting at the barrier would also wait for those)
+      if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(kVmcnt0);
       // row weights h_i = a_i / rho_i (rho_i lies in [2^-120, 2^120] here)
       float h[4];
 #pragma unroll
@@ -826,7 +853,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       // wave stores its share as soon as its own strip is done: one barrier
       // per block
 #pragma unroll
-      for (int e = 0; e < NEWLD; ++e) {
+      for (int e = 0; e < (KDMA ? 0 : NEWLD); ++e) {
         const int idx = tid + e * 512;
         const int row = idx / PER_ROW;
         const int j = jn0 + row;
