@@ -27,7 +27,7 @@ SINKATTN_BF16 = 1
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
             "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate",
             "sinkattn_block_contraction", "sinkattn_timing_enable", "sinkattn_timing_collect",
-            "sinkattn_status_string", "sinkattn_version")
+            "sinkattn_status_string", "sinkattn_last_hip_error", "sinkattn_version")
 
 
 class SinkattnError(RuntimeError):
@@ -82,6 +82,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_timing_collect.restype = i32
     lib.sinkattn_status_string.argtypes = [i32]
     lib.sinkattn_status_string.restype = ctypes.c_char_p
+    lib.sinkattn_last_hip_error.argtypes = []
+    lib.sinkattn_last_hip_error.restype = ctypes.c_char_p
     lib.sinkattn_version.argtypes = []
     lib.sinkattn_version.restype = i32
     if path is None:
@@ -95,7 +97,10 @@ def status_string(status: int) -> str:
 
 def _check(status: int):
     if status != SINKATTN_OK:
-        raise SinkattnError(status, status_string(status))
+        msg = status_string(status)
+        if status == SINKATTN_EHIP:
+            msg += f" ({load_library().sinkattn_last_hip_error().decode()})"
+        raise SinkattnError(status, msg)
 
 
 @dataclass

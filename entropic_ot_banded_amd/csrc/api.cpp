@@ -140,7 +140,19 @@ void timing_mark(hipStream_t st, bool end, int launches) {
 
 using namespace sinkattn;
 
+namespace {
+// the HIP error behind the calling thread's last SINKATTN_EHIP status
+thread_local hipError_t g_last_hip = hipSuccess;
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SINKATTN_OK;
+  g_last_hip = e;
+  return SINKATTN_EHIP;
+}
+}  // namespace
+
 extern "C" {
+
+const char* sinkattn_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
 int sinkattn_version(void) { return 10000; }
 
@@ -171,13 +183,11 @@ int sinkattn_timing_collect(double* total_ms, long long* launches) {
   long long count = 0;
   int status = t.failed ? SINKATTN_EHIP : SINKATTN_OK;
   for (size_t k = 0; k + 1 < t.used; k += 2) {
-    if (hipEventSynchronize(t.pool[k + 1]) != hipSuccess) {
-      status = SINKATTN_EHIP;
-      break;
-    }
+    hipError_t e = hipEventSynchronize(t.pool[k + 1]);
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, t.pool[k], t.pool[k + 1]) != hipSuccess) {
-      status = SINKATTN_EHIP;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.pool[k], t.pool[k + 1]);
+    if (e != hipSuccess) {
+      status = hip_status(e);
       break;
     }
     sum += ms;
@@ -219,7 +229,7 @@ int sinkattn_forward(const void* Q, const void* K, const void* V, int W, int T, 
   FwdLaunch f{Q, K, V, a, b, O, u, v, T, R};
   hipError_t e = launch_forward(g, s->dtype, f, w, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+  return hip_status(e);
 }
 
 int sinkattn_forward_converge(const void* Q, const void* K, const void* V, int W, int T_max, int R,
@@ -242,7 +252,7 @@ int sinkattn_forward_converge(const void* Q, const void* K, const void* V, int W
   f.stop.err_last = err_last;
   hipError_t e = launch_forward(g, s->dtype, f, w, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+  return hip_status(e);
 }
 
 int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T, int R, const float* a,
@@ -263,7 +273,7 @@ int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T,
   BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, vbar0, T, R};
   hipError_t e = launch_backward(g, s->dtype, f, w, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+  return hip_status(e);
 }
 
 int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W, int T, int R_max, const float* a,
@@ -286,7 +296,7 @@ int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W
   BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, nullptr, T, R_max};
   hipError_t e = launch_certificate(g, s->dtype, f, R_max, w, dQ_scratch, dK_scratch, eta, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+  return hip_status(e);
 }
 
 int sinkattn_block_contraction(const void* Q, const void* K, int W, const sinkattn_shape* s, int block,
@@ -300,7 +310,7 @@ int sinkattn_block_contraction(const void* Q, const void* K, int W, const sinkat
   if (block < 1 || block > 128 || block > inside) return SINKATTN_EINVAL;
   hipError_t e = launch_block_diameters(g, s->dtype, Q, K, block, delta, kappa, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return e == hipSuccess ? SINKATTN_OK : SINKATTN_EHIP;
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -445,7 +445,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       if (idx < NWC * PER_ROW) st16(kw + (size_t)(idx / PER_ROW) * RS + (idx % PER_ROW) * 16, kv[e]);
     }
   }
-  float dust_acc = 0.f;  // dustbin-column partial of the segment (thread 0)
+  float dust_acc = 0.f;  // dustbin-column partial of the segment (thread kBlockRows)
 
   // Per-block inputs of the wave's strip, fetched one block ahead: the Q
   // strip (MFMA B operand) and, for the lane's four rows, a_i and the
@@ -484,13 +484,14 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   // Fold block kf's per-wave partials (buffer bf; its window starts at ring
   // slot rbf) into the segment sums in wave order; write out the columns
   // that leave the window after block kf (all of them when `last`).
-  // (threads from kBlockRows on: the first two waves handle the entering
-  // columns instead, which balances the work ahead of the block barrier)
+  // Threads kBlockRows .. kBlockRows + nthr - 1 take the window columns in
+  // turn (the first two waves handle the entering columns instead, which
+  // balances the work ahead of the block barrier).
   static_assert(NWC <= kThreads - kBlockRows, "one window column per folding thread");
   int dir = 1;  // sweep direction of the current step (always forward unless PERS)
-  auto fold = [&](int kf, int bf, int rbf, bool last, bool fwd) {
-    const int wc = tid - kBlockRows;
-    if (wc >= 0 && wc < NWC) {
+  auto fold = [&](int kf, int bf, int rbf, bool last, bool fwd, int nthr) {
+    const int wc0 = tid - kBlockRows;
+    for (int wc = wc0; wc0 >= 0 && wc0 < nthr && wc < NWC; wc += nthr) {
       const int off = wc >> 4;                         // tile offset within block kf's window
       const int c = wrap(rbf + off) * 16 + (wc & 15);  // its ring column
       float s = colsum[c];
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       }
       colsum[c] = s;
     }
-    if (dust && tid == 0) {
+    if (dust && tid == kBlockRows) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
         if (kf * kBlockRows + 16 * w < n) dust_acc += misc[bf * kWaves + w];
@@ -610,16 +611,15 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         vin = gather_v_clamped<PERS>(g, bh, n, j, slo, shi, s_v_prev2(), s_part_in(), p.b, bb, p.sdr);
       }
     };
+
     // ---- partials of the previous block into the segment sums
-    if (bi > 0) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0);
+    if (bi > 0) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0, kThreads - kBlockRows);
 
     // ---- block k: one 16-row strip per wave (all strip values wave-uniform)
     const int i0 = k * kBlockRows + wave * 16;
     if (i0 < n) {
       // Store the entering columns' v from the previous block now, a whole
-      // strip before the next loop top.  (The first two waves hold them; a
-      // strip is skipped only in the segment's last block, after which none
-      // is pending until the final flush.)
+      // strip before the next loop top (the first two waves hold them).
       flush_pending();
       const int sw = wrap(rb + wave);  // ring slot of strip tile t = 0
       const bool partial = i0 + 16 > n;
@@ -830,9 +830,15 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         dp = wave_sum(dp);
         if (lane == 0) misc[buf * kWaves + wave] = dp;
       }
+    } else {
+      // No real rows for this wave: the sequence's partial last block, which
+      // a backward sweep (persistent instance) visits first.  The wave still
+      // loads its share of the next block's inputs.
+      flush_pending();
+#pragma unroll
+      for (int q = 0; q < NPF; ++q) prefetch(q);
+      if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(kVmcnt0);
     }
-    // (a wave without a strip occurs only in a segment's last block, where
-    // no prefetched value is used)
 
     // ---- v^(t-1) of the columns entering with block k + 1 (written to
     // memory during the next strip: a store still in flight at the loop top
@@ -872,7 +878,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   }
     flush_pending();
     // the last block's partials; every column still in the window leaves
-    fold(DIR > 0 ? kend - 1 : b0, (nbs - 1) & 1, rb, true, DIR > 0);
+    fold(DIR > 0 ? kend - 1 : b0, (nbs - 1) & 1, rb, true, DIR > 0, kThreads - kBlockRows);
   };
   for (;;) {
   if constexpr (PERS) {
@@ -931,7 +937,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     }
   }
   }
-  if (dust && tid == 0) p.partd_out[(size_t)bh * g.nseg + seg] = dust_acc;
+  if (dust && tid == kBlockRows) p.partd_out[(size_t)bh * g.nseg + seg] = dust_acc;
 }
 
 // ---------------------------------------------------------------------------

@@ -230,6 +230,11 @@ int sinkattn_timing_collect(double *total_ms, long long *steps);
 /* Human-readable text for a status code (static storage). */
 const char *sinkattn_status_string(int status);
 
+/* Name of the HIP error (hipGetErrorName) behind the calling thread's most
+ * recent SINKATTN_EHIP status, "hipSuccess" if there was none (static
+ * storage; not reset by later successful calls). */
+const char *sinkattn_last_hip_error(void);
+
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int sinkattn_version(void);
 

@@ -208,6 +208,29 @@ def test_long_context_sampled_head():
     del oracle
 
 
+@pytest.mark.parametrize("cfg", ["f32-d16", "bf16-d128", "f32-d64-ragged"])
+def test_multiblock_segments(cfg):
+    """Shapes with more 128-row blocks than workgroups, so each workgroup
+    sweeps a segment of several blocks: the sliding K window, the per-block
+    fold of column partials, the entering columns, and (persistent launch)
+    the direction reversal between steps and the waits on neighbouring
+    segments all run at a size the oracle finishes quickly."""
+    if cfg == "f32-d16":  # 320 blocks: 2-block segments, one per sequence
+        prob, tol = workloads.custom(B=1, H=160, L=256, d=16, W=17, T=20, R=2, seed=11, name=cfg), TOL_F32
+    elif cfg == "bf16-d128":  # 512 blocks: 2-block segments, 4 per sequence
+        prob = workloads.custom(B=1, H=64, L=1024, d=128, W=256, T=8, R=2, dtype="bf16", seed=12, name=cfg)
+        tol = TOL_BF16
+    else:
+        # 640 blocks: 3-block segments (the last one shorter), ragged.  A
+        # partial last block (down to 6 real rows at n = 902, where only the
+        # first wave has rows) is the first block of every backward sweep of
+        # the persistent launch.
+        prob = workloads.custom(B=5, H=16, L=1024, d=64, W=128, T=12, R=2, lengths=[1024, 1000, 902, 700, 333],
+                                seed=13, name=cfg)
+        tol = TOL_F32
+    _check(prob, tol)
+
+
 @pytest.mark.parametrize("cfg", ["tiny", "mid-bf16", "ragged-d128"])
 def test_step_launch_paths_agree(cfg, monkeypatch):
     """Both step schedules: one launch per Sinkhorn step (SINKATTN_STEP_LAUNCHES
