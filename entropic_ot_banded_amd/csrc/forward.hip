@@ -612,9 +612,6 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       }
     };
 
-    // ---- partials of the previous block into the segment sums
-    if (bi > 0) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0, kThreads - kBlockRows);
-
     // ---- block k: one 16-row strip per wave (all strip values wave-uniform)
     const int i0 = k * kBlockRows + wave * 16;
     if (i0 < n) {
@@ -839,6 +836,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       for (int q = 0; q < NPF; ++q) prefetch(q);
       if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(kVmcnt0);
     }
+
+    // ---- partials of the previous block into the segment sums (waves 2
+    // and 3, which finish their strips first; block k + 1 overwrites that
+    // buffer only after the barrier)
+    if (bi > 0 && (wave == 2 || wave == 3)) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0, 2 * 64);
 
     // ---- v^(t-1) of the columns entering with block k + 1 (written to
     // memory during the next strip: a store still in flight at the loop top
