@@ -212,8 +212,10 @@ __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, 
 
 // Steps t_begin .. t_end of one persistent launch (see iter_kernel): the
 // buffers each step reads and writes follow from t, as in the host's launch
-// loop.  progress[bh * nseg + seg] is the last step a segment has finished;
-// *err is set if a neighbour wait gave up (then the results are invalid).
+// loop.  Per segment (index bh * nseg + seg), head is the last step whose
+// starting-end boundary partials it has written and done the last step it
+// has finished; *err is set if a neighbour wait gave up (then the results
+// are invalid).
 struct StepPlan {
   float* part;       // [2][part_slot] column partials (by step parity)
   double* vbuf;      // [2][BHL] v ping-pong
@@ -223,7 +225,8 @@ struct StepPlan {
   size_t part_slot, BHL;
   int T;             // stopped-base steps
   int t_begin, t_end;
-  int* progress;
+  int* head;  // [BH * nseg] last step whose start-side boundary region a segment has written
+  int* done;  // [BH * nseg] last step a segment has finished
   int* err;
 };
 
@@ -268,10 +271,16 @@ constexpr int kMaxSpins = 1 << 20;  // bound of a neighbour wait (each spin slee
 //
 // PERS: one launch runs the steps of a StepPlan (no dustbin).  Sweeps
 // alternate direction, so the ring at the end of a step already holds the
-// window the next step starts with: between steps a workgroup only waits for
-// its two neighbouring segments to finish the step (their partials and v feed
-// its window columns) and finishes v for its window, instead of a new launch
-// reloading the window.  All workgroups must be resident (cooperative launch).
+// window the next step starts with, instead of a new launch reloading it.
+// Every segment sweeps in the same direction in a step, so the neighbour at
+// the end where a sweep finishes began its own sweep at that shared boundary
+// and wrote the partials (and published the v) the next window needs in its
+// first blocks: at a turn a workgroup waits only for that neighbour's head
+// count, then finishes v for its window.  The far neighbour's finished step
+// is awaited later in the sweep, before the first block whose entering
+// columns reach its window; both conditions also keep a segment from
+// overwriting step-parity buffers a neighbour still reads.  All workgroups
+// must be resident (cooperative launch).
 template <typename T, int D, int NT, bool PERS>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan q) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
@@ -532,6 +541,29 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   int rb = 0;                                   // ring slot of block k's first window tile
   int rbp = 0;                                  // same for the previous block
   const int nbs = kend - b0;                    // blocks in the segment
+  // Persistent instance: neighbour handshakes.  A sweep writes the partials
+  // of the columns it shares with the neighbour at its starting end within
+  // its first nb_region blocks (their folds run one block later), and it
+  // needs the far neighbour's previous step only from sweep index bi_far on
+  // (the first block whose entering columns reach that neighbour's window).
+  const int nb_region = (g.TL + g.TR + 7) / 8;
+  const int bi_head = nb_region + 1;  // head(t) is published at the start of this block
+  const int bi_far = nbs - 1 - nb_region;
+  const int me = bh * g.nseg + seg;
+  const bool has_l = seg > 0;
+  const bool has_r = seg + 1 < g.nseg && (seg + 1) * g.SB * kBlockRows < n;
+  // tid 0: wait until cnt_a[ia] >= va (when use_a) and cnt_b[ib] >= vb (when
+  // use_b), with a bounded spin that flags an error instead of hanging
+  auto wait_for = [&](const int* cnt_a, int ia, bool use_a, int va, const int* cnt_b, int ib, bool use_b, int vb) {
+    int spins = 0;
+    while ((use_a && ld_shared<true>(cnt_a + ia) < va) || (use_b && ld_shared<true>(cnt_b + ib) < vb)) {
+      if (++spins > kMaxSpins) {
+        st_shared<true>(q.err, 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  };
   // One sweep over the segment's blocks (DIR = +1 forward, -1 backward: a
   // compile-time direction, so each instantiation keeps one set of indices).
   auto sweep = [&](auto dirc) {
@@ -540,6 +572,10 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     const int k = DIR > 0 ? b0 + bi : kend - 1 - bi;
     const int buf = bi & 1;
     const bool more = bi + 1 < nbs;
+    // the starting-end boundary partials of step t are out (their stores
+    // drained before the last barrier)
+    if constexpr (PERS)
+      if (bi == bi_head && tid == 0) st_shared<true>(q.head + me, t);
     // ---- prefetch for block k + 1 (8 new K tiles, Q strips, a_i, column-
     // finish inputs) in NPF slices, one issued per tile of the strip's first
     // tiles: a wave issuing them all at once stalls on the CU's memory pipe.
@@ -841,6 +877,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     // and 3, which finish their strips first; block k + 1 overwrites that
     // buffer only after the barrier)
     if (bi > 0 && (wave == 2 || wave == 3)) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0, 2 * 64);
+    if constexpr (PERS)  // the region's last fold: its stores complete before the barrier
+      if (bi == bi_head - 1 && (wave == 2 || wave == 3)) __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // ---- v^(t-1) of the columns entering with block k + 1 (written to
     // memory during the next strip: a store still in flight at the loop top
@@ -871,6 +909,15 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       }
       if (ec >= 0) put_w(wrap(rb + NWT + (ec >> 4)) * 16 + (ec & 15), wnew);
     }
+    if constexpr (PERS) {
+      // the far neighbour must have finished step t - 1 before the next block
+      // gathers columns of its window (and before this sweep overwrites the
+      // step t - 1 partials and v^(t-2) it read); the barrier below orders it
+      if (tid == 0 && bi == bi_far - 1 && t > q.t_begin) {
+        const bool far_r = DIR < 0;  // a backward sweep ends at the left neighbour
+        wait_for(q.done, far_r ? me + 1 : me - 1, far_r ? has_r : has_l, t - 1, q.done, 0, false, 0);
+      }
+    }
     __syncthreads();
     if (more) {
       cur = nxt;
@@ -894,29 +941,24 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   } else {
     if (t == q.t_end) break;
     // ---- next step: publish this segment's progress (every store of step t
-    // is complete), wait for the neighbouring segments, then finish v^(t) for
+    // is complete), wait for the neighbour at this end, then finish v^(t) for
     // the window the new sweep starts with (its K rows are in the ring)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-      const int me = bh * g.nseg + seg;
-      st_shared<true>(q.progress + me, t);
-      const bool has_l = seg > 0;
-      const bool has_r = seg + 1 < g.nseg && (seg + 1) * g.SB * kBlockRows < n;
-      int spins = 0;
-      while ((has_l && ld_shared<true>(q.progress + me - 1) < t) ||
-             (has_r && ld_shared<true>(q.progress + me + 1) < t)) {
-        if (++spins > kMaxSpins) {
-          st_shared<true>(q.err, 1);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-      }
-    }
-    __syncthreads();
+    const bool right = dir > 0;  // this sweep ended at the right neighbour
     ++t;
     dir = -dir;
-    set_step();
+    if (tid == 0) {
+      st_shared<true>(q.done + me, t - 1);
+      if (bi_head >= nbs) st_shared<true>(q.head + me, t - 1);
+      set_step();  // nothing reads the step's pointers until the barrier below
+      // The next sweep starts at this end: the neighbour there must have
+      // written its starting-end region of step t - 1 (its sweep began at the
+      // shared boundary).  A short segment also needs the far neighbour now.
+      const bool far_now = bi_far < 1;
+      wait_for(q.head, right ? me + 1 : me - 1, right ? has_r : has_l, t - 1, q.done, right ? me - 1 : me + 1,
+               far_now && (right ? has_l : has_r), t - 1);
+    }
     __syncthreads();
     vref = s_v_prev2() ? ld_shared<true>(s_v_prev2() + bh * L + seg_r0) : 0.0;
     {
@@ -1726,7 +1768,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, ikp, 512, iter_lds);
     if (err != hipSuccess) return err;
     if (coop && (long long)per * cus >= iter_grid) {
-      const int nprog = nbh * g.nseg + 1;
+      const int nprog = 2 * nbh * g.nseg + 1;
       hipLaunchKernelGGL(fill_int, dim3((nprog + 255) / 256), dim3(256), 0, st, w.prog, nprog, 0);
       IterArgs a{};
       a.Q = f.Q;
@@ -1737,7 +1779,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       a.sdc = w.sdc;
       a.padded_grid = iter_grid;
       StepPlan q{w.part, w.vbuf, w.ubuf, w.tail_u, w.tail_v, part_slot, BHL, f.T, 1, N, w.prog,
-                 w.prog + nbh * g.nseg};
+                 w.prog + nbh * g.nseg, w.prog + 2 * nbh * g.nseg};
       Geom gg = g;
       void* args[] = {&gg, &a, &q};
       if (timing_enabled()) timing_mark(st, false);
@@ -1808,7 +1850,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     hipLaunchKernelGGL((output_kernel<T, D>), dim3(grid), dim3(512), out_lds, st, g, o);
   }
   if (persistent)
-    hipLaunchKernelGGL(step_wait_failed, dim3(1), dim3(1), 0, st, w.prog + nbh * g.nseg, f.O, f.u);
+    hipLaunchKernelGGL(step_wait_failed, dim3(1), dim3(1), 0, st, w.prog + 2 * nbh * g.nseg, f.O, f.u);
   if (g.dustbin) {
     hipLaunchKernelGGL(dustbin_output<T>, dim3(nbh), dim3(128), 0, st, g, reinterpret_cast<const T*>(f.V),
                        w.tail_v + (size_t)f.R * BHL, o.dstate, w.sdr, f.O, f.u, f.v);

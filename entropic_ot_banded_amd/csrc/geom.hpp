@@ -63,7 +63,7 @@ struct Workspace {
   float* bw;       // backward vectors [(3R + 8) * BHL]
   double* err;     // [BH] base convergence check (row-marginal L1 error)
   double* red;     // [kRedParts][2] + [kMaxCertR + 1][4] norm reductions of the tail certificate
-  int* prog;       // [BH * nseg + 1] persistent step kernel: last step per segment, then an error flag
+  int* prog;       // [2 * BH * nseg + 1] persistent step kernel: per-segment head and done steps, then an error flag
   size_t floats;
 };
 
@@ -91,7 +91,7 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.bw = take((size_t)(3 * R + 8) * BHL);
   w.err = take_d(BH);
   w.red = take_d(2 * kRedParts + 4 * (kMaxCertR + 1));
-  w.prog = reinterpret_cast<int*>(take(BH * (size_t)g.nseg + 1));
+  w.prog = reinterpret_cast<int*>(take(2 * BH * (size_t)g.nseg + 1));
   w.floats = off;
   return w;
 }
