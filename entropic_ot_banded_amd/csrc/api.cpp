@@ -265,8 +265,8 @@ int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T,
   Geom g;
   int st = make_geom(s, W, &g);
   if (st != SINKATTN_OK) return st;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) ||
-      !aligned16(dV) || !aligned16(workspace))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
+      !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
     return SINKATTN_EINVAL;
   Workspace w = carve(static_cast<float*>(workspace), g, R);
   if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
@@ -288,8 +288,8 @@ int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W
   Geom g;
   int st = make_geom(s, W, &g);
   if (st != SINKATTN_OK) return st;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) ||
-      !aligned16(dV) || !aligned16(dQ_scratch) || !aligned16(dK_scratch) || !aligned16(workspace))
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
+      !aligned16(dK) || !aligned16(dV) || !aligned16(dQ_scratch) || !aligned16(dK_scratch) || !aligned16(workspace))
     return SINKATTN_EINVAL;
   Workspace w = carve(static_cast<float*>(workspace), g, R_max);
   if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;

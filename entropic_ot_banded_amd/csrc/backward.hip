@@ -525,19 +525,27 @@ __global__ __launch_bounds__(256) void bw_col_kernel(Geom g, BwArgs p) {
 constexpr int kTokPerBlock = 16;  // 256 threads
 
 // D_i = dO_i . O_i on active rows.
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bw_rowdot(Geom g, const T* dO, const float* O, float* Dv) {
+  constexpr int V = D / 16;  // contiguous elements per lane (16 lanes per token; one vector load each)
   const int bh = blockIdx.y;
   const int i = blockIdx.x * kTokPerBlock + (threadIdx.x >> 4);
-  const int c0 = threadIdx.x & 15;
+  const int c0 = (threadIdx.x & 15) * V;
   const int n = real_len(g, bh / g.H);
   const int nact = n + (g.dustbin ? 1 : 0);
   const size_t o = (size_t)bh * g.L + (i < g.L ? i : 0);
   float s = 0.f;
-  if (i < nact)
-    for (int c = c0; c < g.d; c += 16) s = __builtin_fmaf(Elt<T>::load(dO, o * g.d + c), O[o * g.d + c], s);
+  if (i < nact) {
+    // rows are 16-byte aligned (checked at the boundary) and c0 is a multiple of V
+    T a[V];
+    float b[V];
+    __builtin_memcpy(a, __builtin_assume_aligned(dO + o * D + c0, V * sizeof(T)), sizeof(a));
+    __builtin_memcpy(b, __builtin_assume_aligned(O + o * D + c0, V * sizeof(float)), sizeof(b));
+#pragma unroll
+    for (int c = 0; c < V; ++c) s = __builtin_fmaf(Elt<T>::load(a, c), b[c], s);
+  }
   s = row16_sum(s);
-  if (i < g.L && c0 == 0) Dv[o] = s;
+  if (i < g.L && (threadIdx.x & 15) == 0) Dv[o] = s;
 }
 
 // After the dV sweep: add the dustbin-row entry (delta, j) for real j, zero
@@ -1208,7 +1216,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   const T* dOt = reinterpret_cast<const T*>(f.dO);
   if (g.dustbin) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
   const dim3 tok((g.L + kTokPerBlock - 1) / kTokPerBlock, nbh);
-  hipLaunchKernelGGL(bw_rowdot<T>, tok, dim3(256), 0, st, g, dOt, f.O, Dv);
+  hipLaunchKernelGGL((bw_rowdot<T, D>), tok, dim3(256), 0, st, g, dOt, f.O, Dv);
   // bf16 with d >= 64: streamed sweeps (one workgroup per 128-index block)
   constexpr bool kSweep = sizeof(T) == 2 && D >= 64;
   const int sgrid = (nbh * ceil_div_pos(g.L, 128) + 7) & ~7;
