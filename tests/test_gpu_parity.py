@@ -208,7 +208,7 @@ def test_long_context_sampled_head():
     del oracle
 
 
-@pytest.mark.parametrize("cfg", ["f32-d16", "bf16-d128", "f32-d64-ragged"])
+@pytest.mark.parametrize("cfg", ["f32-d16", "bf16-d128", "f32-d64-ragged", "bf16-d128-ragged", "bf16-d64-w64-ragged"])
 def test_multiblock_segments(cfg):
     """Shapes with more 128-row blocks than workgroups, so each workgroup
     sweeps a segment of several blocks: the sliding K window, the per-block
@@ -219,6 +219,14 @@ def test_multiblock_segments(cfg):
         prob, tol = workloads.custom(B=1, H=160, L=256, d=16, W=17, T=20, R=2, seed=11, name=cfg), TOL_F32
     elif cfg == "bf16-d128":  # 512 blocks: 2-block segments, 4 per sequence
         prob = workloads.custom(B=1, H=64, L=1024, d=128, W=256, T=8, R=2, dtype="bf16", seed=12, name=cfg)
+        tol = TOL_BF16
+    elif cfg == "bf16-d128-ragged":  # 512 blocks: 2-block segments, partial last blocks (LDS-DMA ring fill)
+        prob = workloads.custom(B=2, H=32, L=1024, d=128, W=256, T=8, R=2, dtype="bf16", lengths=[1000, 650],
+                                seed=14, name=cfg)
+        tol = TOL_BF16
+    elif cfg == "bf16-d64-w64-ragged":  # 640 blocks: 3-block segments, 5-tile strips, register ring fill
+        prob = workloads.custom(B=4, H=20, L=1024, d=64, W=64, T=12, R=2, dtype="bf16",
+                                lengths=[1024, 990, 520, 130], seed=15, name=cfg)
         tol = TOL_BF16
     else:
         # 640 blocks: 3-block segments (the last one shorter), ragged.  A
