@@ -107,14 +107,21 @@ __device__ __forceinline__ DustC load_dust(const Geom& g, int bh, const double* 
 // (column partials, published v): device-scope when COH (the persistent step
 // kernel, whose steps run in one launch: no cache may serve a stale copy),
 // plain otherwise.
+// (COH accesses name the global address space explicitly: their pointers
+// may have been read from LDS, and flat accesses would also count against
+// the LDS wait counter, forcing full waits on the LDS reads around them.)
+template <typename X>
+__device__ __forceinline__ __attribute__((address_space(1))) X* gmem(X* p) {
+  return (__attribute__((address_space(1))) X*)p;
+}
 template <bool COH, typename X>
 __device__ __forceinline__ X ld_shared(const X* p) {
-  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (COH) return __hip_atomic_load(gmem(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else return *p;
 }
 template <bool COH, typename X>
 __device__ __forceinline__ void st_shared(X* p, X v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (COH) __hip_atomic_store(gmem(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;
 }
 
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   auto publish_v = [&](int j, double vj) {
     if (s_v_out() && j >= seg_r0 && j < seg_r1) {
       st_shared<PERS>(s_v_out() + bh * L + j, vj);
-      if (s_v_tail()) s_v_tail()[bh * L + j] = vj;
+      if (s_v_tail()) gmem(s_v_tail())[bh * L + j] = vj;
     }
   };
   auto wrap = [](int x) { return x >= RING ? x - RING : x; };  // x in [0, 2 RING)
@@ -832,7 +839,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           const int i = i0 + 4 * lg + rsel;
           const double u = (double)log2f(av / rsv) - (double)shv - vref;
           s_u_out()[bh * L + i] = u;
-          if (s_u_tail()) s_u_tail()[bh * L + i] = u;
+          if (s_u_tail()) gmem(s_u_tail())[bh * L + i] = u;
         }
       }
       // column partials of this strip, sum_i e_ij h_i, reduced over the four
