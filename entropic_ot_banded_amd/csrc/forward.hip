@@ -129,9 +129,11 @@ __device__ __forceinline__ void st_shared(X* p, X v) {
 // not make the wave wait for the data.  Column j lies in the windows of the
 // segments [slo, shi].
 template <bool COH = false>
+// own_seg >= 0: that segment's partial is `own` (the caller holds it) instead
+// of being loaded.
 __device__ __forceinline__ VIn gather_v_range(const Geom& g, int bh, int n, int j, int slo, int shi,
                                               const double* v_prev2, const float* part_in, const float* b,
-                                              int bb, const float* sdr) {
+                                              int bb, const float* sdr, int own_seg = -1, float own = 0.f) {
   const size_t L = g.L;
   const int segw = g.SB * kBlockRows;
   VIn r;
@@ -142,7 +144,8 @@ __device__ __forceinline__ VIn gather_v_range(const Geom& g, int bh, int n, int 
     const int sg = slo + k;
     r.part[k] = 0.f;
     if (sg <= shi && sg * segw < n)  // segments without real rows wrote nothing
-      r.part[k] = ld_shared<COH>(part_in + ((size_t)bh * g.nseg + sg) * g.SW + (j - (sg * segw - 16 * g.TL)));
+      r.part[k] = sg == own_seg ? own
+                                : ld_shared<COH>(part_in + ((size_t)bh * g.nseg + sg) * g.SW + (j - (sg * segw - 16 * g.TL)));
   }
   r.sdr = g.dustbin ? sdr[bh * L + j] : 0.f;
   r.valid = (2u << kMaxSeg) - 1;
@@ -192,10 +195,11 @@ __device__ __forceinline__ void window_segments(const Geom& g, int j, int& slo, 
 
 template <bool COH = false>
 __device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
-                                        const float* part_in, const float* b, int bb, const float* sdr) {
+                                        const float* part_in, const float* b, int bb, const float* sdr,
+                                        int own_seg = -1, float own = 0.f) {
   int slo, shi;
   window_segments(g, j, slo, shi);
-  return gather_v_range<COH>(g, bh, n, j, slo, shi, v_prev2, part_in, b, bb, sdr);
+  return gather_v_range<COH>(g, bh, n, j, slo, shi, v_prev2, part_in, b, bb, sdr, own_seg, own);
 }
 
 // v^(t-1)_j = v^(t-2)_j + log2(b_j / gamma_j), gamma_j = sum_i P^(t-1,t-2)_ij
@@ -526,7 +530,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       if ((fwd ? off < 8 : off >= NWT - 8) || last) {
         const int j = (kf * 8 - g.TL + off) * 16 + (wc & 15);
         st_shared<PERS>(s_part_out() + ((size_t)bh * g.nseg + seg) * g.SW + (j - cs), s);
-        s = 0.f;
+        // a sweep's last fold leaves its sums in place: the next step's
+        // window (this one) takes the segment's own partials from here
+        if (!last) s = 0.f;
       }
       colsum[c] = s;
     }
@@ -947,24 +953,35 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     break;
   } else {
     if (t == q.t_end) break;
-    // ---- next step: publish this segment's progress (every store of step t
-    // is complete), wait for the neighbour at this end, then finish v^(t) for
-    // the window the new sweep starts with (its K rows are in the ring)
-    __builtin_amdgcn_s_waitcnt(0);
+    // ---- next step: wait for the neighbour at this end, then finish v^(t)
+    // for the window the new sweep starts with (its K rows are in the ring).
+    // A segment of more than a few blocks publishes done(t) only at the end
+    // of the turn: its own partials of the window come from LDS, so the last
+    // fold's stores drain while the turn runs.  A short one (which may need
+    // the far neighbour now) publishes first, so that no two turns wait on
+    // each other.
+    const bool short_seg = bi_far < 1 || bi_head >= nbs;
+    if (short_seg) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool right = dir > 0;  // this sweep ended at the right neighbour
     ++t;
     dir = -dir;
     if (tid == 0) {
-      st_shared<true>(q.done + me, t - 1);
-      if (bi_head >= nbs) st_shared<true>(q.head + me, t - 1);
-      set_step();  // nothing reads the step's pointers until the barrier below
+      if (short_seg) {
+        st_shared<true>(q.done + me, t - 1);
+        if (bi_head >= nbs) st_shared<true>(q.head + me, t - 1);
+      }
       // The next sweep starts at this end: the neighbour there must have
       // written its starting-end region of step t - 1 (its sweep began at the
-      // shared boundary).  A short segment also needs the far neighbour now.
+      // shared boundary).  Its first poll is issued ahead of set_step.
+      const bool has_e = right ? has_r : has_l;
+      const int e_idx = right ? me + 1 : me - 1;
+      const int e0 = has_e ? ld_shared<true>(q.head + e_idx) : t;
+      set_step();  // nothing reads the step's pointers until the barrier below
       const bool far_now = bi_far < 1;
-      wait_for(q.head, right ? me + 1 : me - 1, right ? has_r : has_l, t - 1, q.done, right ? me - 1 : me + 1,
-               far_now && (right ? has_l : has_r), t - 1);
+      if (e0 < t - 1 || far_now)
+        wait_for(q.head, e_idx, has_e, t - 1, q.done, right ? me - 1 : me + 1, far_now && (right ? has_l : has_r),
+                 t - 1);
     }
     __syncthreads();
     vref = s_v_prev2() ? ld_shared<true>(s_v_prev2() + bh * L + seg_r0) : 0.0;
@@ -972,8 +989,14 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       const int kc = dir > 0 ? b0 : kend - 1;  // the block the new sweep starts at
       const int jc = (kc * 8 - g.TL) * 16 + tid;
       const bool colok = tid < NWC && jc >= 0 && jc < n;
+      const int c = wrap(rb + (tid >> 4)) * 16 + (tid & 15);  // its ring column
+      float own = 0.f;
+      if (tid < NWC) {
+        own = colsum[c];  // this segment's partial (the last fold's sum)
+        colsum[c] = 0.f;
+      }
       VIn pin;
-      if (colok && s_part_in()) pin = gather_v<true>(g, bh, n, jc, s_v_prev2(), s_part_in(), p.b, bb, p.sdr);
+      if (colok && s_part_in()) pin = gather_v<true>(g, bh, n, jc, s_v_prev2(), s_part_in(), p.b, bb, p.sdr, seg, own);
       if (tid < NWC) {
         float w = kNegInf;
         if (colok) {
@@ -981,10 +1004,13 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           publish_v(jc, vj);
           w = (float)(vj - vref);
         }
-        put_w(wrap(rb + (tid >> 4)) * 16 + (tid & 15), w);
+        put_w(c, w);
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (!short_seg && tid == 0) {
+        st_shared<true>(q.done + me, t - 1);  // every store of step t - 1 has drained
+      }
     }
   }
   }
