@@ -208,7 +208,7 @@ def forward(Q, K, V, W: int, T: int, R: int, a, b, lengths=None, dustbin: bool =
     shape = _shape_of(Q, lengths, dustbin)
     nbytes = workspace_bytes(shape, W, R)
     if nbytes == 0:
-        raise SinkattnError(SINKATTN_EINVAL, "invalid shape/W/R")
+        raise SinkattnError(SINKATTN_EINVAL, "invalid or unsupported shape/W/R (see the envelope in sinkattn.h)")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
     B, H, L, d = Q.shape
@@ -236,7 +236,7 @@ def forward_converge(Q, K, V, W: int, T_max: int, R: int, a, b, tol: float, chec
     shape = _shape_of(Q, lengths, dustbin)
     nbytes = workspace_bytes(shape, W, R)
     if nbytes == 0:
-        raise SinkattnError(SINKATTN_EINVAL, "invalid shape/W/R")
+        raise SinkattnError(SINKATTN_EINVAL, "invalid or unsupported shape/W/R (see the envelope in sinkattn.h)")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
     B, H, L, d = Q.shape

@@ -74,9 +74,10 @@ typedef enum { SINKATTN_F32 = 0, SINKATTN_BF16 = 1 } sinkattn_dtype;
  *                and column are active against every active token (corner
  *                included).  Requires n_b < L.
  * Supported envelope of this build: d in {16, 32, 64} for fp32 and
- * {32, 64, 128} for bf16; band tile count ceil(W/2 / 16) + floor((15 +
- * ceil(W/2) - 1) / 16) + 1 <= 17 (W <= 257), or W >= 2L - 1 with L <= 256.
- * Anything else returns SINKATTN_EUNSUPPORTED. */
+ * {32, 64, 128} for bf16; band tile count ceil(h1 / 16) + ceil(h2 / 16) + 1
+ * <= 17 with h1 = min(floor(W/2), L-1) and h2 = min(ceil(W/2) - 1, L-1):
+ * every W <= 257, and any W (the dense case W >= 2L - 1 included) when
+ * L <= 129.  Anything else returns SINKATTN_EUNSUPPORTED. */
 typedef struct {
   int32_t B, H, L, d;
   int32_t dtype;

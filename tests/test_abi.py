@@ -75,6 +75,17 @@ def test_workspace_rejects_invalid(lib):
     assert eoba.workspace_bytes(_shape(dustbin=True), 64, 2) == 0   # dustbin needs lengths
 
 
+def test_band_envelope(lib):
+    """The half-widths are clamped to L - 1 and at most 17 tiles of 16 fit: any W
+    up to 257, and dense bands (W >= 2L - 1) only while L <= 129."""
+    assert eoba.workspace_bytes(_shape(), 257, 2) > 0
+    assert eoba.workspace_bytes(_shape(), 258, 2) == 0
+    assert eoba.workspace_bytes(_shape(L=129), 2 * 129 - 1, 2) > 0
+    assert eoba.workspace_bytes(_shape(L=129), 10000, 2) > 0
+    assert eoba.workspace_bytes(_shape(L=130), 2 * 130 - 1, 2) == 0
+    assert eoba.workspace_bytes(_shape(L=185), 2 * 185 - 1, 2) == 0
+
+
 def test_tail_offsets(lib):
     s = _shape(L=100)
     BHL = 1 * 2 * 100

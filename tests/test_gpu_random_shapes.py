@@ -1,0 +1,81 @@
+"""Seeded random shapes through the C-ABI against the float64 oracle.
+
+Each case draws the element type, head dimension, band width (up to 256,
+dense W = 2L - 1 for L <= 129, and the diagonal W = 1), length, batch and
+heads (half of the cases with more 128-row blocks than workgroups, so every
+workgroup sweeps a multi-block segment), ragged lengths (empty or at least 8
+tokens), the dustbin, T and R.  The cases stay small enough for the oracle;
+the seed list is fixed, so a failure names its case.  Tolerances are the
+parity bounds of test_gpu_parity.py.  With W = 1 the scores do not affect O
+(P_ii = a_i), so dQ = dK = 0 exactly: those two get an absolute bound against
+the scale of dV instead of a relative one.  Sequences of one or two tokens
+are left out: their potentials are tiny, and the fp32 rounding each step adds
+in the neutral direction (u + c, v - c) dominates a relative error there.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_util import compare, log, run_gpu, run_oracle
+from tests.test_gpu_parity import TOL_BF16, TOL_F32
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(16))
+
+
+def random_case(seed: int) -> workloads.Problem:
+    rng = np.random.default_rng(1000 + seed)
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    d = int(rng.choice([32, 64, 128] if dtype == "bf16" else [16, 32, 64]))
+    if seed % 2 == 0:  # more blocks than workgroups (256): multi-block segments
+        L = int(rng.integers(600, 1100))
+        nblk = -(-L // 128)
+        B = int(rng.integers(1, 4))
+        H = -(-(-(-300 // nblk) + int(rng.integers(0, 24))) // B)
+        W = int(rng.choice([17, 64, 100, 128, 200, 256]))
+        T = int(rng.integers(1, 7))
+    else:
+        L = int(rng.integers(8, 700))
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 5))
+        widths = [1, 17, 33, 64, 128, 256] + ([2 * L - 1] if L <= 129 else [])
+        W = int(rng.choice(widths))
+        T = int(rng.integers(0, 15))
+    R = int(rng.integers(0, 5))
+    ragged = rng.random() < 0.6
+    dustbin = bool(ragged and rng.random() < 0.4)
+    lengths = None
+    if ragged:  # empty sequences, or at least 8 tokens
+        hi = L - 1 if dustbin else L
+        lengths = [0 if rng.random() < 0.15 else int(rng.integers(min(8, hi), hi + 1)) for _ in range(B)]
+    return workloads.custom(B=B, H=H, L=L, d=d, W=W, T=T, R=R, dtype=dtype, seed=2000 + seed,
+                            lengths=lengths, dustbin=dustbin, name=f"random-{seed}")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import entropic_ot_banded_amd as eoba
+    eoba.load_library()  # fail loudly if the HIP library is missing
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_shape(seed):
+    prob = random_case(seed)
+    tol = TOL_F32 if prob.dtype == "f32" else TOL_BF16
+    log(f"[random] {prob.name} dtype={prob.dtype} shape={prob.shape} W={prob.W} T={prob.T} R={prob.R} "
+        f"lengths={None if prob.lengths is None else list(prob.lengths)} dustbin={prob.dustbin}")
+    gpu = run_gpu(prob)
+    ref = run_oracle(prob)
+    errs = compare(gpu, ref, prob)
+    log("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        if prob.W == 1 and k in ("dQ", "dK"):
+            scale = np.linalg.norm(gpu["dV"])
+            assert np.linalg.norm(gpu[k]) <= 1e-5 * (scale if scale > 0 else 1.0), k
+            continue
+        assert v <= tol[k], f"{prob.name}: {k} rel err {v:.3e} > {tol[k]:.1e}"
