@@ -798,6 +798,26 @@ __global__ void dustbin_scores_bw(Geom g, const T* Q, const T* K, float* sdr, fl
 // 128-bit reads of 8 consecutive rows and the transposed reads of 4
 // consecutive rows are free of bank conflicts.
 // ---------------------------------------------------------------------------
+// LDS address (byte offset in the workgroup's LDS) of a pointer into it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// One wave-wide LDS DMA: lane l copies 16 bytes from base + off (its own
+// off) to LDS bytes [lds + 16 l, lds + 16 l + 16).  Written as inline asm so
+// that the compiler does not treat the transposed LDS reads of the sweeps as
+// possibly aliasing a DMA in flight (it would wait for every DMA before
+// them); the sweeps order their DMAs and reads with explicit waits and
+// barriers.  No register is written.  `lds` and `base` are wave-uniform.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory", "m0");
+}
+
 constexpr int kSwWaves = 8;
 constexpr int kSwThreads = 64 * kSwWaves;
 
@@ -810,6 +830,7 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   constexpr int NTEN = MODE == 0 ? 1 : 2;   // streamed tensors
   constexpr int PT = MODE == 2 ? 1 : 0;     // streamed tensor of the product
   constexpr int TBYTES = 32 * RB;     // one tile pair of one tensor
+  constexpr int NBUF = 4;             // pair buffers: three pairs in flight ahead of the one in use
   static_assert(CPR >= 8, "the chunk swizzle needs 8 chunks per row");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -851,10 +872,10 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
 
-  // LDS: tiles [2 buffers][NTEN][32 rows][RB] | wv [NWC] | window vectors [NV][NWC]
+  // LDS: tiles [NBUF buffers][NTEN][32 rows][RB] | wv [NWC] | window vectors [NV][NWC]
   constexpr int NVMAX = 2 * kMaxR;
   char* tbuf = smem;
-  float* wv = reinterpret_cast<float*>(smem + 2 * NTEN * TBYTES);
+  float* wv = reinterpret_cast<float*>(smem + NBUF * NTEN * TBYTES);
   float* vec = wv + NWC;
   const int NV = MODE == 0 ? 1 : (MODE == 1 ? 2 * R : 0);
 
@@ -901,33 +922,44 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   // or, for dV, the product side (dO)
   const char* X0 = reinterpret_cast<const char*>(COL ? p.Q : p.K) + (size_t)bh * L * RB;
   const char* X1 = reinterpret_cast<const char*>(COL ? p.dO : p.V) + (size_t)bh * L * RB;
-  // one 16-byte chunk per thread per tensor and pair (rows clamped into
-  // [0, L); rows outside [0, n) are stored as zeros)
-  u4 pre[NTEN];
-  int pre_row = 0;
-  auto load_pair = [&](int pp) {
-    const int idx = tid;  // < 32 * CPR when CPR == 16; guarded otherwise
-    const int r32 = idx / CPR;
-    int grow = (tw0 + 2 * pp) * 16 + r32;
-    pre_row = grow;
-    grow = grow < 0 ? 0 : (grow >= (int)L ? (int)L - 1 : grow);
-    if (idx < 32 * CPR) {
-      pre[0] = ld16(X0 + (size_t)grow * RB + (idx % CPR) * 16);
-      if (NTEN > 1) pre[NTEN - 1] = ld16(X1 + (size_t)grow * RB + (idx % CPR) * 16);
+  // Pairs stream into LDS by DMA (global_load_lds, 16 bytes per lane): wave
+  // w fills bytes [w KB, (w + 1) KB) of each tensor's pair buffer, i.e. rows
+  // RPW w .. RPW (w + 1) - 1, and the lane at chunk position pc of its row
+  // loads logical chunk pc ^ f(row), which leaves the buffer in the swizzled
+  // layout the reads expect (sw_chunk is an involution).  Rows outside the
+  // sequence are loaded from the nearest real row: every entry they feed is
+  // masked to exactly zero (their scores are -inf).
+  constexpr int RPW = 1024 / RB;                  // rows per wave instruction
+  const uint32_t lds_base = lds_addr(tbuf);
+  constexpr int DMA_WAVES = 32 / RPW;             // waves that move a pair
+  const bool dma_wave = wave < DMA_WAVES;
+  auto issue_pair = [&](int pp) {
+    if (dma_wave) {
+      const int pos = lane * 16;
+      const int r32 = wave * RPW + pos / RB;
+      const int c = sw_chunk((pos % RB) / 16, r32);
+      int row = (tw0 + 2 * pp) * 16 + r32;
+      row = row < 0 ? 0 : (row >= n ? n - 1 : row);
+      const uint32_t dst = lds_base + (uint32_t)((pp % NBUF) * NTEN) * TBYTES + wave * 1024;
+      const uint32_t off = (uint32_t)(row * RB + c * 16);
+      lds_dma16(X0, off, dst);
+      if (NTEN > 1) lds_dma16(X1, off, dst + TBYTES);
     }
   };
-  auto store_pair = [&](int buf) {
-    const int idx = tid;
-    if (idx < 32 * CPR) {
-      const int r32 = idx / CPR, c16 = idx % CPR;
-      const bool ok = pre_row >= 0 && pre_row < n;
-      const int off = r32 * RB + sw_chunk(c16, r32) * 16;
-#pragma unroll
-      for (int te = 0; te < NTEN; ++te) {
-        const u4 v = ok ? pre[te] : (u4){0u, 0u, 0u, 0u};
-        st16(tbuf + (size_t)(buf * NTEN + te) * TBYTES + off, v);
-      }
-    }
+  // Barrier of the pair pipeline: this wave's LDS reads are done and its
+  // DMAs of the next pair have landed (at most `later` pairs issued after it
+  // still in flight: vmcnt counts this wave's DMA instructions, and the loop
+  // issues no other vector memory operation), then the waves meet.  A plain
+  // __syncthreads would also wait for every DMA in flight, draining the
+  // prefetch at each pair.
+  auto pipe_barrier = [&](int later) {
+    asm volatile("" ::: "memory");
+    constexpr int kLgkm0 = 0x0070;  // lgkmcnt(0), expcnt left free; vmcnt in bits 3:0
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(kLgkm0 | (2 * NTEN));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(kLgkm0 | NTEN);
+    else __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // strip operands (registers): score side (Q rows / K rows), dP side (dO / V)
@@ -987,20 +1019,16 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
 #pragma unroll
   for (int ds = 0; ds < ND; ++ds) acc[ds] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  load_pair(0);
-  store_pair(0);
-  if (NP > 1) load_pair(1);
-  __syncthreads();
+  for (int q = 0; q < 3 && q < NP; ++q) issue_pair(q);
+  pipe_barrier((NP - 1 < 2) ? NP - 1 : 2);  // pair 0 (pairs 1, 2 may still be in flight)
 
   const int wstart = wave;           // first window tile of this strip
   const int sidx0 = s0b + wave * 16;  // first strip index of the wave
   const bool wactive = sidx0 < n;
   for (int pp = 0; pp < NP; ++pp) {
-    const int buf = pp & 1;
-    if (pp + 1 < NP) {
-      store_pair(buf ^ 1);             // pair pp + 1 (loaded one step ago)
-      if (pp + 2 < NP) load_pair(pp + 2);
-    }
+    const int buf = pp % NBUF;
+    // pair pp + 3 into the buffer pair pp - 1 used (every wave is past it)
+    if (pp + 3 < NP) issue_pair(pp + 3);
     // tiles 2pp, 2pp + 1 of the window; strip-relative t = window tile - wave
     float val[2][4];
     bool any = false;
@@ -1077,7 +1105,9 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
         acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], lo, bv);
       }
     }
-    __syncthreads();
+    // pair pp + 1 complete in every wave before the next iteration reads it
+    const int later = NP - 2 - pp;  // pairs issued after pair pp + 1
+    pipe_barrier(later < 0 ? 0 : (later > 2 ? 2 : later));
   }
 
   if (!wactive) {
@@ -1228,7 +1258,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     const int NWC = 2 * NP * 16;
     const int ntens = mode == 0 ? 1 : 2;
     const int nv = mode == 0 ? 1 : (mode == 1 ? 2 * R : 0);
-    return (size_t)2 * ntens * 32 * D * 2 + (size_t)NWC * 4 * (1 + nv) + 64;
+    return (size_t)4 * ntens * 32 * D * 2 + (size_t)NWC * 4 * (1 + nv) + 64;  // 4 pair buffers
   };
   if constexpr (kSweep) {
 #define SET_SW(COLV, MODEV, RMV)                                                                        \
