@@ -798,26 +798,6 @@ __global__ void dustbin_scores_bw(Geom g, const T* Q, const T* K, float* sdr, fl
 // 128-bit reads of 8 consecutive rows and the transposed reads of 4
 // consecutive rows are free of bank conflicts.
 // ---------------------------------------------------------------------------
-// LDS address (byte offset in the workgroup's LDS) of a pointer into it.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// One wave-wide LDS DMA: lane l copies 16 bytes from base + off (its own
-// off) to LDS bytes [lds + 16 l, lds + 16 l + 16).  Written as inline asm so
-// that the compiler does not treat the transposed LDS reads of the sweeps as
-// possibly aliasing a DMA in flight (it would wait for every DMA before
-// them); the sweeps order their DMAs and reads with explicit waits and
-// barriers.  No register is written.  `lds` and `base` are wave-uniform.
-__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds), "v"(off), "s"(base)
-      : "memory", "m0");
-}
-
 constexpr int kSwWaves = 8;
 constexpr int kSwThreads = 64 * kSwWaves;
 

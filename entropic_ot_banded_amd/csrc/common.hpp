@@ -161,6 +161,26 @@ __device__ __forceinline__ int sw_chunk(int chunk, int row) {
   return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
 }
 
+// LDS address (byte offset in the workgroup's LDS) of a pointer into it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// One wave-wide LDS DMA: lane l copies 16 bytes from base + off (its own
+// off) to LDS bytes [lds + 16 l, lds + 16 l + 16).  Written as inline asm so
+// that the compiler does not treat the transposed LDS reads of the streamed
+// sweeps as possibly aliasing a DMA in flight (it would wait for every DMA
+// before them); the sweeps order their DMAs and reads with explicit waits and
+// barriers.  No register is written.  `lds` and `base` are wave-uniform.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory", "m0");
+}
+
 __device__ __forceinline__ u2 ld_tr16(const char* p) {
   typedef short s4v __attribute__((ext_vector_type(4)));
   const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(p));

@@ -1458,8 +1458,9 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
   const int NP = (NW + 1) >> 1;
   const int NWC = 2 * NP * 16;
   const int tw0 = blk * 8 - g.TL;
-  char* tbuf = smem;                                        // [2][2 tensors][32 rows][RB]
-  float* wv = reinterpret_cast<float*>(smem + 4 * TBYTES);  // [NWC] v_j - vref
+  constexpr int NBUF = 4;                                          // pair buffers: three pairs in flight
+  char* tbuf = smem;                                               // [NBUF][2 tensors][32 rows][RB]
+  float* wv = reinterpret_cast<float*>(smem + NBUF * 2 * TBYTES);  // [NWC] v_j - vref
 
   if (tid == 0)
     sh_vref = p.part_in ? finish_v(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr) : 0.0;
@@ -1482,31 +1483,43 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
 
   const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
   const char* Vb = reinterpret_cast<const char*>(p.V) + (size_t)bh * L * RB;
-  u4 pre[2];
-  int pre_row = 0;
-  auto load_pair = [&](int pp) {
-    const int r32 = tid / CPR;
-    int grow = (tw0 + 2 * pp) * 16 + r32;
-    pre_row = grow;
-    grow = grow < 0 ? 0 : (grow >= (int)L ? (int)L - 1 : grow);
-    if (tid < 32 * CPR) {
-      pre[0] = ld16(Kb + (size_t)grow * RB + (tid % CPR) * 16);
-      pre[1] = ld16(Vb + (size_t)grow * RB + (tid % CPR) * 16);
-    }
-  };
-  auto store_pair = [&](int buf) {
-    if (tid < 32 * CPR) {
-      const int r32 = tid / CPR, c16 = tid % CPR;
-      const bool ok = pre_row >= 0 && pre_row < n;
-      const int off = r32 * RB + sw_chunk(c16, r32) * 16;
-#pragma unroll
-      for (int te = 0; te < 2; ++te)
-        st16(tbuf + (size_t)(buf * 2 + te) * TBYTES + off, ok ? pre[te] : (u4){0u, 0u, 0u, 0u});
-    }
-  };
-
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // K and V tile pairs stream into LDS by DMA, three pairs ahead: wave w
+  // fills bytes [w KB, (w + 1) KB) of each tensor's pair buffer, and the lane
+  // at chunk position pc of its row loads logical chunk pc ^ f(row), leaving
+  // the swizzled layout the reads expect.  Rows outside the sequence are
+  // loaded from the nearest real row (their scores are masked to -inf, so
+  // every product they enter is exactly zero).
+  constexpr int RPW = 1024 / RB;  // rows per wave instruction
+  const bool dma_wave = wave < 32 / RPW;
+  const uint32_t lds_base = lds_addr(tbuf);
+  auto issue_pair = [&](int pp) {
+    if (dma_wave) {
+      const int pos = lane * 16;
+      const int r32 = wave * RPW + pos / RB;
+      const int c = sw_chunk((pos % RB) / 16, r32);
+      int row = (tw0 + 2 * pp) * 16 + r32;
+      row = row < 0 ? 0 : (row >= n ? n - 1 : row);
+      const uint32_t dst = lds_base + (uint32_t)((pp % NBUF) * 2) * TBYTES + wave * 1024;
+      const uint32_t off = (uint32_t)(row * RB + c * 16);
+      lds_dma16(Kb, off, dst);
+      lds_dma16(Vb, off, dst + TBYTES);
+    }
+  };
+  // this wave's LDS reads done and its DMAs of the next pair landed (at most
+  // `later` pairs after it in flight; the loop issues no other vector memory
+  // operation), then the waves meet (a plain __syncthreads would wait for
+  // every DMA in flight)
+  auto pipe_barrier = [&](int later) {
+    asm volatile("" ::: "memory");
+    constexpr int kLgkm0 = 0x0070;  // lgkmcnt(0), expcnt left free; vmcnt in bits 3:0
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(kLgkm0 | 4);
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(kLgkm0 | 2);
+    else __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   const int i0 = r0 + wave * 16;
   const int si = i0 + lr;
   const bool sok = si < n;
@@ -1535,17 +1548,13 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
 #pragma unroll
   for (int ds = 0; ds < ND; ++ds) oacc[ds] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  load_pair(0);
-  store_pair(0);
-  if (NP > 1) load_pair(1);
-  __syncthreads();
+  for (int q = 0; q < 3 && q < NP; ++q) issue_pair(q);
+  pipe_barrier((NP - 1 < 2) ? NP - 1 : 2);  // pair 0
   const bool wactive = i0 < n;
   for (int pp = 0; pp < NP; ++pp) {
-    const int buf = pp & 1;
-    if (pp + 1 < NP) {
-      store_pair(buf ^ 1);
-      if (pp + 2 < NP) load_pair(pp + 2);
-    }
+    const int buf = pp % NBUF;
+    // pair pp + 3 into the buffer pair pp - 1 used (every wave is past it)
+    if (pp + 3 < NP) issue_pair(pp + 3);
     float val[2][4];
     bool any = false;
 #pragma unroll
@@ -1591,7 +1600,8 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
         oacc[ds] = Elt<bf16_t>::mma_chunk(oacc[ds], lo, bv);
       }
     }
-    __syncthreads();
+    const int later = NP - 2 - pp;  // pairs issued after pair pp + 1
+    pipe_barrier(later < 0 ? 0 : (later > 2 ? 2 : later));
   }
   if (!wactive) return;
   // dustbin column term for real rows: P_i,delta V_delta
@@ -1874,7 +1884,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   o.padded_grid = grid;
   if constexpr (sizeof(T) == 2 && D >= 64) {
     const int NP = (g.NT + kWaves) / 2;
-    const size_t sweep_lds = (size_t)4 * 32 * D * 2 + (size_t)2 * NP * 16 * 4 + 64;
+    const size_t sweep_lds = (size_t)8 * 32 * D * 2 + (size_t)2 * NP * 16 * 4 + 64;  // 4 pair buffers of K and V
     err = hipFuncSetAttribute(reinterpret_cast<const void*>(output_sweep_kernel<D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds);
     if (err != hipSuccess) return err;
