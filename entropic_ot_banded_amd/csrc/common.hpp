@@ -171,6 +171,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // sweeps as possibly aliasing a DMA in flight (it would wait for every DMA
 // before them); the sweeps order their DMAs and reads with explicit waits and
 // barriers.  No register is written.  `lds` and `base` are wave-uniform.
+// M0 (a reserved register, so its clobber is only advisory) is overwritten:
+// the kernels that use this helper have no other M0 user (the compiler sets
+// M0 only for its own LDS-DMA builtins and indirect register moves, neither
+// of which they contain).
 __device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
