@@ -145,6 +145,9 @@ PROF_ARGS = "--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contracti
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $REPO/gpurun_out/prof/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
              + PROF_ARGS)
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
+               "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+SQ_FILE = os.path.join(ROOT, "profiles", "iter_kernel_long_context_sq.txt")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
            "-d $REPO/gpurun_out/prof/{sub} -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 "
            + PROF_ARGS + " --copy-calibration")
@@ -224,6 +227,53 @@ def summarize(d):
         with open(PMC_FILE, "w") as f:
             json.dump(pmc, f, indent=1)
     with open(TRACE_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    summarize_sq(d)
+
+
+def summarize_sq(d):
+    """Issue counters of the fused step kernel from one rocprofv3 --pmc pass
+    (d/sq), per Sinkhorn step, set against the algorithmic work of a step."""
+    import glob
+    files = glob.glob(os.path.join(d, "sq", "*counter_collection.csv"))
+    if not files:
+        return
+    per = {}
+    for r in _csv_rows(files[0]):
+        if "iter_kernel" not in r["Kernel_Name"]:
+            continue
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+        per.setdefault(key, {})[r["Counter_Name"]] = (per.get(key, {}).get(r["Counter_Name"], 0.0)
+                                                      + float(r["Counter_Value"]))
+    if not per:
+        return
+    names = SQ_COUNTERS.split()
+    avg = {c: sum(v.get(c, 0.0) / steps_per_dispatch(k[1]) for k, v in per.items()) / len(per) for c in names}
+    step_omega = work_counts(1, 8, 32768, 128, 256, 1, 0)[0]  # band entries of one step, all 8 heads
+    cycles = avg["GRBM_GUI_ACTIVE"] / 8  # summed over the 8 XCDs
+    simds = 256 * 4
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv "
+           "-d $REPO/gpurun_out/prof/sq -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 " + PROF_ARGS)
+    lines = ["Issue counters of the fused step kernel (iter_kernel), long-context workload",
+             "(B=1, H=8, L=32768, d=128, W=256, T=100, R=2, bf16), per Sinkhorn step, averaged over "
+             f"{len(per)} dispatches:", "", "Command ($REPO = repository root):", "  " + cmd,
+             "  python3 $REPO/bench.py --summarize $REPO/gpurun_out/prof", ""]
+    for c in names:
+        lines.append(f"  {c:32s} {avg[c]:16.0f}")
+    mfma_busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * simds) if cycles else float("nan")
+    flops_hw = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    lines += ["",
+              f"  active cycles per step (GRBM_GUI_ACTIVE / 8 XCDs): {cycles:.0f}",
+              f"  MFMA pipe busy: {mfma_busy:.3f} of {simds} SIMDs x active cycles",
+              f"  bf16 MFMA flops counted: {flops_hw / 1e9:.2f} G per step; algorithmic 2 d |Omega| = "
+              f"{2 * 128 * step_omega / 1e9:.2f} G (ratio {flops_hw / (2 * 128 * step_omega):.3f}: tile overcompute)",
+              f"  exp (v_exp_f32 and other f32 transcendentals) x 64 lanes: {avg['SQ_INSTS_VALU_TRANS_F32'] * 64 / 1e6:.1f} M "
+              f"per step; band entries |Omega| = {step_omega / 1e6:.1f} M",
+              f"  VALU instructions per band entry x 64 lanes: {avg['SQ_INSTS_VALU'] * 64 / step_omega:.2f}",
+              f"  LDS instructions per step: {avg['SQ_INSTS_LDS'] / 1e6:.2f} M",
+              f"  kernel sources hash {kernel_source_hash()}"]
+    with open(SQ_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -409,6 +459,10 @@ def main():
         y.copy_(x)
         torch.cuda.synchronize()
 
+    # Sustained bf16 MFMA and v_exp_f32 rates on this GPU (after the timed
+    # region): the roofline fractions are also given against these.
+    peaks = eoba.measure_peaks(dev) if prob.dtype == "bf16" else None
+
     ms_per_step = ms_total / args.steps
     tokens = prob.real_tokens()
     value = tokens / (ms_per_step * 1e-3)
@@ -440,6 +494,16 @@ def main():
             "survey_counting": {"flops": sv_flops, "exps": sv_exps,
                                 "frac": round(max(sv_flops / peak, sv_exps / PEAK_EXP) / t_s, 4)},
             "peak_mfma_flops": peak, "peak_exp_per_s": PEAK_EXP}
+    if peaks is not None:
+        pm, pe = peaks["mfma_bf16_flops"], peaks["exp_per_s"]
+        roofline["mfma_frac_measured"] = round(step_flops / avg_step_s / pm, 4)
+        roofline["exp_frac_measured"] = round(omega / avg_step_s / pe, 4)
+        path["executed"]["frac_measured"] = round(max(ex_flops / pm, ex_exps / pe) / t_s, 4)
+        path["survey_counting"]["frac_measured"] = round(max(sv_flops / pm, sv_exps / pe) / t_s, 4)
+        path["measured_peaks"] = {"mfma_bf16_flops": float(f"{pm:.4g}"), "exp_per_s": float(f"{pe:.4g}"),
+                                  "clock_ghz": round(peaks["clock_hz"] / 1e9, 3),
+                                  "probe": "sinkattn_measure_peaks: v_mfma_f32_16x16x32_bf16 and v_exp_f32 "
+                                           "issue rates with every CU loaded"}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -7,7 +7,7 @@ autograd wrapper; torch supplies device memory and streams only.
 
 from .binding import (  # noqa: F401
     EXPORTED, SINKATTN_BF16, SINKATTN_F32, Shape, SinkattnError, backward, block_contraction, forward,
-    forward_converge, load_library, select_tail_depth, status_string, tail_certificate, tail_offset,
+    forward_converge, load_library, measure_peaks, select_tail_depth, status_string, tail_certificate, tail_offset,
     tail_stack, timing_collect, timing_enable, workspace_bytes,
 )
 from .autograd import sinkhorn_attention  # noqa: F401

@@ -27,7 +27,8 @@ SINKATTN_BF16 = 1
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
             "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate",
             "sinkattn_block_contraction", "sinkattn_timing_enable", "sinkattn_timing_collect",
-            "sinkattn_status_string", "sinkattn_last_hip_error", "sinkattn_version")
+            "sinkattn_status_string", "sinkattn_last_hip_error", "sinkattn_version",
+            "sinkattn_measure_peaks")
 
 
 class SinkattnError(RuntimeError):
@@ -86,6 +87,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_last_hip_error.restype = ctypes.c_char_p
     lib.sinkattn_version.argtypes = []
     lib.sinkattn_version.restype = i32
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.sinkattn_measure_peaks.argtypes = [dp, dp, dp, vp]
+    lib.sinkattn_measure_peaks.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -321,6 +325,19 @@ def block_contraction(Q, K, W: int, block: int, lengths=None, dustbin: bool = Fa
                                                    _ptr(kappa), _stream(Q.device))
     _check(st)
     return delta, kappa
+
+
+def measure_peaks(device=None) -> dict:
+    """Sustained bf16 score-MFMA flop/s, v_exp_f32 results/s and the shader
+    clock on `device` (see sinkattn_measure_peaks); blocks for about 50 ms."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    mfma, ex, clk = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    with torch.cuda.device(dev):
+        st = load_library().sinkattn_measure_peaks(ctypes.byref(mfma), ctypes.byref(ex), ctypes.byref(clk),
+                                                   _stream(dev))
+    _check(st)
+    return {"mfma_bf16_flops": mfma.value, "exp_per_s": ex.value, "clock_hz": clk.value}
 
 
 def select_tail_depth(eta, tau: float) -> int:

@@ -20,6 +20,7 @@ hipError_t launch_block_diameters(const Geom& g, int dtype, const void* Q, const
                                   float* kappa, hipStream_t st);
 hipError_t launch_certificate(const Geom& g, int dtype, const BwdLaunch& base, int R_max, const Workspace& w,
                               float* dQs, float* dKs, double* eta, hipStream_t st);
+hipError_t launch_peak_probes(double* mfma_flops, double* exps, double* clock_hz, hipStream_t st);
 
 namespace {
 
@@ -311,6 +312,11 @@ int sinkattn_block_contraction(const void* Q, const void* K, int W, const sinkat
   hipError_t e = launch_block_diameters(g, s->dtype, Q, K, block, delta, kappa, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
   return hip_status(e);
+}
+
+int sinkattn_measure_peaks(double* mfma_bf16_flops, double* exp_per_s, double* clock_hz, hipStream_t stream) {
+  if (!mfma_bf16_flops || !exp_per_s) return SINKATTN_EINVAL;
+  return hip_status(launch_peak_probes(mfma_bf16_flops, exp_per_s, clock_hz, stream));
 }
 
 }  // extern "C"

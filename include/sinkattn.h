@@ -228,6 +228,20 @@ int sinkattn_block_contraction(const void *Q, const void *K, int W, const sinkat
 int sinkattn_timing_enable(int on);
 int sinkattn_timing_collect(double *total_ms, long long *steps);
 
+/* Measured peaks for roofline fractions.  Runs two probes on `stream`,
+ * each one untimed short launch and one timed launch of about 10 ms that
+ * fill every CU, and waits for them (blocking):
+ *   mfma_bf16_flops : out, sustained flop/s of v_mfma_f32_16x16x32_bf16, the
+ *                     bf16 score / P.V instruction (2 * 16 * 16 * 32 flops each);
+ *   exp_per_s       : out, sustained v_exp_f32 results per second (the one
+ *                     exp2 per band entry of every pass);
+ *   clock_hz        : optional out (may be NULL), the shader clock during the
+ *                     MFMA probe (s_memtime over s_memrealtime; 0 if unknown).
+ * Allocates no device memory.  Returns SINKATTN_EINVAL on NULL required
+ * outputs, SINKATTN_EHIP on a launch or event failure. */
+int sinkattn_measure_peaks(double *mfma_bf16_flops, double *exp_per_s, double *clock_hz,
+                           hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char *sinkattn_status_string(int status);
 
