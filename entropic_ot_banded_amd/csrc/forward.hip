@@ -165,10 +165,13 @@ __device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, in
   VIn r;
   // v^(t-2) = 0 when v_prev2 is null: load from `b` instead (any readable
   // address; the finish ignores it), so no branch sits before the loads
+  // (per-(b, h) base pointers with unsigned 32-bit lane offsets: j >= 0)
+  const uint32_t ju = (uint32_t)j;
   const double* vp = v_prev2 ? v_prev2 + bh * L : reinterpret_cast<const double*>(b);
-  r.vprev = ld_shared<COH>(vp + (v_prev2 ? j : 0));
-  r.b = b[(size_t)bb * L + j];
+  r.vprev = ld_shared<COH>(vp + (v_prev2 ? ju : 0u));
+  r.b = (b + (size_t)bb * L)[ju];
   r.valid = v_prev2 ? 1u << kMaxSeg : 0u;
+  const float* pb = part_in + (size_t)bh * g.nseg * g.SW;
 #pragma unroll
   for (int k = 0; k < kMaxSeg; ++k) {
     const int sg = slo + k;
@@ -176,10 +179,10 @@ __device__ __forceinline__ VIn gather_v_clamped(const Geom& g, int bh, int n, in
     const int sgc = sg < g.nseg ? sg : g.nseg - 1;
     int off = j - (sgc * segw - 16 * g.TL);
     off = off < 0 ? 0 : (off >= g.SW ? g.SW - 1 : off);
-    r.part[k] = ld_shared<COH>(part_in + ((size_t)bh * g.nseg + sgc) * g.SW + off);
+    r.part[k] = ld_shared<COH>(pb + (uint32_t)(sgc * g.SW + off));
     r.valid |= (ok ? 1u : 0u) << k;
   }
-  r.sdr = sdr[bh * L + j];  // always allocated; used only with a dustbin
+  r.sdr = (sdr + bh * L)[ju];  // always allocated; used only with a dustbin
   return r;
 }
 
@@ -290,8 +293,11 @@ constexpr int kMaxSpins = 1 << 20;  // bound of a neighbour wait (each spin slee
 // count, then finishes v for its window.  The far neighbour's finished step
 // is awaited later in the sweep, before the first block whose entering
 // columns reach its window; both conditions also keep a segment from
-// overwriting step-parity buffers a neighbour still reads.  All workgroups
-// must be resident (cooperative launch).
+// overwriting step-parity buffers a neighbour still reads.  This covers every
+// segment whose partials a window column needs only when a segment spans at
+// least the band's 16 (TL + TR) columns (then the windows of segments two
+// apart are disjoint); the host launches this instance only then.  All
+// workgroups must be resident (cooperative launch).
 template <typename T, int D, int NT, bool PERS>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan q) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
@@ -647,7 +653,19 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         int j = jp0 + ec;
         int slo, shi;
         if constexpr (PERS) {
-          window_segments(g, j, slo, shi);
+          // the segment windows holding j (as window_segments): the 128
+          // entering columns are consecutive and a segment spans at least
+          // 128, so each bound is the block's first column's plus 0 or 1
+          // (one block-uniform division per bound instead of two per lane)
+          const int segw = g.SB * kBlockRows;
+          const int xb = jp0 + 16 * g.TL;  // >= 0
+          const int h0 = xb / segw;
+          const int l0 = floor_div(xb - g.SW, segw);
+          const int x = xb + ec;
+          shi = h0 + (x >= (h0 + 1) * segw ? 1 : 0);
+          shi = shi > g.nseg - 1 ? g.nseg - 1 : shi;
+          slo = l0 + 1 + (x - g.SW >= (l0 + 1) * segw ? 1 : 0);
+          slo = slo < 0 ? 0 : slo;
           j = j < 0 ? 0 : j;
         } else {
           const int segw = g.SB * kBlockRows;
@@ -1801,9 +1819,14 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   const int N = f.T + f.R;
   // Every step in one cooperative launch of the persistent instance, when all
   // its workgroups fit on the device at once (no dustbin, no early stop; set
-  // SINKATTN_STEP_LAUNCHES to launch once per step instead).
+  // SINKATTN_STEP_LAUNCHES to launch once per step instead), and when a
+  // segment is at least as wide as the band's tile span: the persistent
+  // kernel synchronises a segment with its two neighbours only, and with
+  // narrower segments the windows of segments two apart overlap, so a turn
+  // would read partial sums of a segment it never waited for.
   bool persistent = false;
-  if (N >= 2 && !g.dustbin && !stop_early && !std::getenv("SINKATTN_STEP_LAUNCHES")) {
+  if (N >= 2 && !g.dustbin && !stop_early && g.SB * kBlockRows >= 16 * (g.TL + g.TR) &&
+      !std::getenv("SINKATTN_STEP_LAUNCHES")) {
     int dev = 0, coop = 0, cus = 0, per = 0;
     err = hipGetDevice(&dev);
     if (err == hipSuccess) err = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);

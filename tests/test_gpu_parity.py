@@ -251,7 +251,9 @@ def test_step_launch_paths_agree(cfg, monkeypatch):
     elif cfg == "mid-bf16":
         prob, tol = workloads.make(2, dtype="bf16"), TOL_BF16
     else:
-        prob = workloads.custom(B=2, H=2, L=1500, d=128, W=256, T=9, R=2, dtype="bf16",
+        # 384 blocks: 2-block segments, as wide as the band's tile span (the
+        # narrowest segments the persistent launch takes at W = 256)
+        prob = workloads.custom(B=2, H=16, L=1500, d=128, W=256, T=9, R=2, dtype="bf16",
                                 lengths=[1500, 1111], seed=7, name="ragged-d128")
         tol = TOL_BF16
     monkeypatch.setenv("SINKATTN_STEP_LAUNCHES", "1")
