@@ -54,3 +54,26 @@ def test_forward_is_deterministic(name, schedule, monkeypatch):
     for r in runs[1:]:
         for k, x, y in zip("Ouv", runs[0], r):
             assert np.array_equal(x, y, equal_nan=True), f"{name} {schedule}: {k} differs between calls"
+
+
+@pytest.mark.parametrize("name", ["sb1-w256-ragged", "sb2-w256-ragged", "sb1-w64"])
+def test_backward_is_deterministic(name):
+    c = CASES[name]
+    print(f"case: {name} backward", flush=True)
+    prob = workloads.custom(B=c["B"], H=c["H"], L=c["L"], d=c["d"], W=c["W"], T=c["T"], R=2, dtype="bf16",
+                            lengths=c["lengths"], seed=7, name=name)
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16).contiguous()
+    Q, K, V, dO = up(prob.Q), up(prob.K), up(prob.V), up(prob.dO)
+    a = torch.from_numpy(prob.a).to(dev)
+    b = torch.from_numpy(prob.b).to(dev)
+    lengths = None if c["lengths"] is None else torch.tensor(prob.lengths, dtype=torch.int32, device=dev)
+    O, u, v, ws = eoba.forward(Q, K, V, c["W"], c["T"], 2, a, b, lengths=lengths)
+    runs = []
+    for _ in range(3):
+        grads = eoba.backward(Q, K, V, c["W"], c["T"], 2, a, b, O, dO, ws, lengths=lengths)
+        torch.cuda.synchronize()
+        runs.append([g.cpu().numpy() for g in grads[:3]])
+    for r in runs[1:]:
+        for k, x, y in zip(("dQ", "dK", "dV"), runs[0], r):
+            assert np.array_equal(x, y, equal_nan=True), f"{name}: {k} differs between calls"
