@@ -77,3 +77,46 @@ def test_backward_is_deterministic(name):
     for r in runs[1:]:
         for k, x, y in zip(("dQ", "dK", "dV"), runs[0], r):
             assert np.array_equal(x, y, equal_nan=True), f"{name}: {k} differs between calls"
+
+
+def _random_case(seed):
+    """Shapes on both sides of the persistent launch's segment-width bound:
+    segments of 1-4 blocks (SB), W up to 256, ragged lengths, both dtypes."""
+    rng = np.random.default_rng(5000 + seed)
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    d = int(rng.choice([64, 128] if dtype == "bf16" else [16, 32, 64]))
+    sb = int(rng.integers(1, 5))
+    L = int(rng.integers(300, 1400))
+    nblk = -(-L // 128)
+    B = int(rng.integers(1, 3))
+    # B H nblk blocks over 256 workgroups gives segments of sb blocks
+    H = max(1, -(-(256 * (sb - 1) + 1) // (B * nblk)))
+    W = int(rng.choice([33, 64, 128, 200, 256]))
+    lengths = [int(rng.integers(L // 2, L + 1)) for _ in range(B)] if rng.random() < 0.6 else None
+    return dict(B=B, H=H, L=L, d=d, W=W, T=int(rng.integers(4, 13)), lengths=lengths, dtype=dtype)
+
+
+@pytest.mark.parametrize("seed", list(range(10)))
+def test_random_shapes_deterministic(seed):
+    c = _random_case(seed)
+    print(f"case: random-{seed} {c}", flush=True)
+    prob = workloads.custom(B=c["B"], H=c["H"], L=c["L"], d=c["d"], W=c["W"], T=c["T"], R=2, dtype=c["dtype"],
+                            lengths=c["lengths"], seed=9000 + seed, name=f"det-random-{seed}")
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(tdt).contiguous()
+    Q, K, V, dO = up(prob.Q), up(prob.K), up(prob.V), up(prob.dO)
+    a = torch.from_numpy(prob.a).to(dev)
+    b = torch.from_numpy(prob.b).to(dev)
+    lengths = None if c["lengths"] is None else torch.tensor(prob.lengths, dtype=torch.int32, device=dev)
+    runs, ws = [], None
+    for _ in range(3):
+        if ws is not None:
+            ws.zero_()
+        O, u, v, ws = eoba.forward(Q, K, V, c["W"], c["T"], 2, a, b, lengths=lengths, workspace=ws)
+        dQ, dK, dV, _ = eoba.backward(Q, K, V, c["W"], c["T"], 2, a, b, O, dO, ws, lengths=lengths)
+        torch.cuda.synchronize()
+        runs.append([x.cpu().numpy() for x in (O, u, v, dQ, dK, dV)])
+    for r in runs[1:]:
+        for k, x, y in zip(("O", "u", "v", "dQ", "dK", "dV"), runs[0], r):
+            assert np.array_equal(x, y, equal_nan=True), f"random-{seed}: {k} differs between calls"
