@@ -120,3 +120,38 @@ def test_random_shapes_deterministic(seed):
     for r in runs[1:]:
         for k, x, y in zip(("O", "u", "v", "dQ", "dK", "dV"), runs[0], r):
             assert np.array_equal(x, y, equal_nan=True), f"random-{seed}: {k} differs between calls"
+
+
+@pytest.mark.parametrize("variant", ["dustbin", "converge"])
+def test_dustbin_and_early_stop_deterministic(variant):
+    print(f"case: {variant}", flush=True)
+    if variant == "dustbin":
+        prob = workloads.custom(B=2, H=4, L=1100, d=64, W=128, T=10, R=2, dtype="bf16", lengths=[1099, 700],
+                                dustbin=True, seed=31, name="det-dustbin")
+    else:
+        prob = workloads.custom(B=2, H=4, L=1100, d=64, W=128, T=60, R=2, dtype="bf16", lengths=[1100, 800],
+                                seed=32, name="det-converge")
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16).contiguous()
+    Q, K, V, dO = up(prob.Q), up(prob.K), up(prob.V), up(prob.dO)
+    a = torch.from_numpy(prob.a).to(dev)
+    b = torch.from_numpy(prob.b).to(dev)
+    lengths = torch.tensor(prob.lengths, dtype=torch.int32, device=dev)
+    runs, ws = [], None
+    for _ in range(3):
+        if ws is not None:
+            ws.zero_()
+        if variant == "dustbin":
+            O, u, v, ws = eoba.forward(Q, K, V, prob.W, prob.T, 2, a, b, lengths=lengths, dustbin=True, workspace=ws)
+            T_used = prob.T
+        else:
+            O, u, v, ws, T_used, _ = eoba.forward_converge(Q, K, V, prob.W, prob.T, 2, a, b, 1e-3, check_every=3,
+                                                           lengths=lengths, workspace=ws)
+        dQ, dK, dV, _ = eoba.backward(Q, K, V, prob.W, T_used, 2, a, b, O, dO, ws, lengths=lengths,
+                                      dustbin=variant == "dustbin")
+        torch.cuda.synchronize()
+        runs.append([T_used] + [x.cpu().numpy() for x in (O, u, v, dQ, dK, dV)])
+    for r in runs[1:]:
+        assert r[0] == runs[0][0], f"{variant}: base length differs between calls"
+        for k, x, y in zip(("O", "u", "v", "dQ", "dK", "dV"), runs[0][1:], r[1:]):
+            assert np.array_equal(x, y, equal_nan=True), f"{variant}: {k} differs between calls"
