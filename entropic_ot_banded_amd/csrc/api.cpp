@@ -41,6 +41,11 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
   if (s->dustbin && !s->lengths) return SINKATTN_EINVAL;  // dustbin index n_b needs n_b < L
   const long long bhl = (long long)s->B * s->H * s->L;
   if (bhl * s->d > (long long)INT_MAX * 4 || bhl > INT_MAX) return SINKATTN_EUNSUPPORTED;
+  // per-(b, h) kernels index B H on the grid's y dimension (at most 65535)
+  if ((long long)s->B * s->H > 65535) return SINKATTN_EUNSUPPORTED;
+  // row offsets within one (b, h) slice of Q, K, V, dO are 32-bit
+  const long long esize = s->dtype == SINKATTN_BF16 ? 2 : 4;
+  if ((long long)s->L * s->d * esize > INT_MAX) return SINKATTN_EUNSUPPORTED;
   if (!dtype_d_supported(s->dtype, s->d)) return SINKATTN_EUNSUPPORTED;
   Geom x{};
   x.B = s->B;

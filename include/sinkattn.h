@@ -77,7 +77,9 @@ typedef enum { SINKATTN_F32 = 0, SINKATTN_BF16 = 1 } sinkattn_dtype;
  * {32, 64, 128} for bf16; band tile count ceil(h1 / 16) + ceil(h2 / 16) + 1
  * <= 17 with h1 = min(floor(W/2), L-1) and h2 = min(ceil(W/2) - 1, L-1):
  * every W <= 257, and any W (the dense case W >= 2L - 1 included) when
- * L <= 129.  Anything else returns SINKATTN_EUNSUPPORTED. */
+ * L <= 129; sizes B H <= 65535, B H L <= 2^31 - 1, B H L d <= 4 (2^31 - 1)
+ * and one (b, h) slice of Q under 2 GiB (L d bytes-per-element <= 2^31 - 1).
+ * Anything else returns SINKATTN_EUNSUPPORTED. */
 typedef struct {
   int32_t B, H, L, d;
   int32_t dtype;

@@ -120,6 +120,14 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, _shape(d=40)) == binding.SINKATTN_EUNSUPPORTED
     assert _fwd(lib, _shape(B=0)) == binding.SINKATTN_EINVAL
     assert _fwd(lib, sh, ws_bytes=1024) == binding.SINKATTN_EWORKSPACE
+    # size envelope: B H <= 65535, B H L <= 2^31 - 1, B H L d <= 4 (2^31 - 1),
+    # one (b, h) slice under 2 GiB
+    assert _fwd(lib, _shape(B=1, H=1, L=2 ** 24, d=128, dtype=binding.SINKATTN_BF16)) == \
+        binding.SINKATTN_EUNSUPPORTED
+    assert _fwd(lib, _shape(B=256, H=256, L=8)) == binding.SINKATTN_EUNSUPPORTED
+    assert _fwd(lib, _shape(B=1, H=2, L=2 ** 30)) == binding.SINKATTN_EUNSUPPORTED
+    assert _fwd(lib, _shape(B=1, H=4, L=2 ** 27, d=128, dtype=binding.SINKATTN_BF16)) == \
+        binding.SINKATTN_EUNSUPPORTED
 
 
 def test_forward_converge_validation_before_launch(lib):
