@@ -141,7 +141,7 @@ def load_pmc(launch_units=None):
     return (fetch + write) * 1024.0
 
 
-PROF_ARGS = "--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0"
+PROF_ARGS = "--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0 --no-peaks"
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $REPO/gpurun_out/prof/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
              + PROF_ARGS)
@@ -315,6 +315,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--R", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA/exp peak probes")
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -461,7 +462,7 @@ def main():
 
     # Sustained bf16 MFMA and v_exp_f32 rates on this GPU (after the timed
     # region): the roofline fractions are also given against these.
-    peaks = eoba.measure_peaks(dev) if prob.dtype == "bf16" else None
+    peaks = eoba.measure_peaks(dev) if prob.dtype == "bf16" and not args.no_peaks else None
 
     ms_per_step = ms_total / args.steps
     tokens = prob.real_tokens()
