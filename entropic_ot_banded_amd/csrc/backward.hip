@@ -1039,6 +1039,10 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
         }
         // lane: strip index si, window indices wi = tg * 16 + 4 lg + r
         const int cw = wt * 16 + 4 * lg;  // window position of r = 0
+        // wave-uniform: every entry of the tile lies inside the band and
+        // between real rows and columns, so no entry needs the mask
+        const int olo = COL ? sidx0 - tg * 16 - 15 : tg * 16 - sidx0 - 15;  // lowest j - i
+        const bool inner = olo >= -g.h1 && olo + 30 <= g.h2 && sidx0 + 16 <= n && tg * 16 + 16 <= n;
         const f4 w4 = *reinterpret_cast<const f4*>(wv + cw);
         f4 z4 = {0.f, 0.f, 0.f, 0.f};
         if (MODE == 0) z4 = *reinterpret_cast<const f4*>(vec + cw);
@@ -1047,7 +1051,7 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
           const int wi = tg * 16 + 4 * lg + r;
           const int o = COL ? si - wi : wi - si;  // j - i
           float x = __builtin_fmaf(sacc[r], g.scale2, w4[r] + sbias);
-          x = (o >= -g.h1 && o <= g.h2 && sok && wi >= 0 && wi < n) ? x : kNegInf;
+          if (!inner) x = (o >= -g.h1 && o <= g.h2 && sok && wi >= 0 && wi < n) ? x : kNegInf;
           const float pe = exp2_fast(x);
           if (MODE == 0) {
             val[tt][r] = pe * z4[r];

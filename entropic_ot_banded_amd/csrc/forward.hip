@@ -1594,12 +1594,16 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
         }
         const int cw = wt * 16 + 4 * lg;
         const f4 w4 = *reinterpret_cast<const f4*>(wv + cw);
+        // wave-uniform: every entry of the tile lies inside the band and
+        // between real rows and columns, so no entry needs the mask
+        const int olo = tg * 16 - i0 - 15;  // lowest j - i of the tile
+        const bool inner = olo >= -g.h1 && olo + 30 <= g.h2 && i0 + 16 <= n && tg * 16 + 16 <= n;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int wj = tg * 16 + 4 * lg + r;
           const int o = wj - si;
           float x = __builtin_fmaf(sacc[r], g.scale2, w4[r] + ui2);
-          x = (o >= -g.h1 && o <= g.h2 && sok && wj >= 0 && wj < n) ? x : kNegInf;
+          if (!inner) x = (o >= -g.h1 && o <= g.h2 && sok && wj >= 0 && wj < n) ? x : kNegInf;
           val[tt][r] = exp2_fast(x);
         }
       }
