@@ -1046,6 +1046,12 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
         const f4 w4 = *reinterpret_cast<const f4*>(wv + cw);
         f4 z4 = {0.f, 0.f, 0.f, 0.f};
         if (MODE == 0) z4 = *reinterpret_cast<const f4*>(vec + cw);
+        // window modifiers of the lane's four entries, one 16-byte read each
+        // (cw is a multiple of 4 and NWC of 16)
+        f4 mv[2 * RM];
+#pragma unroll
+        for (int k = 0; k < 2 * RM; ++k)
+          if (MODE == 1 && k < 2 * R) mv[k] = *reinterpret_cast<const f4*>(vec + (size_t)k * NWC + cw);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int wi = tg * 16 + 4 * lg + r;
@@ -1062,8 +1068,8 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
 #pragma unroll
             for (int k = 0; k < RM; ++k) {
               if (k < R) {
-                const float m0 = vec[(size_t)(2 * k) * NWC + cw + r];
-                const float m1 = vec[(size_t)(2 * k + 1) * NWC + cw + r];
+                const float m0 = mv[2 * k][r];
+                const float m1 = mv[2 * k + 1][r];
                 br -= COL ? m0 * sm0[k] : sm0[k] * m0;
                 br -= COL ? m1 * sm1[k] : sm1[k] * m1;
               }
