@@ -193,18 +193,25 @@ __device__ __forceinline__ u2 ld_tr16(const char* p) {
   return r;
 }
 
+// Two floats to packed bf16 (element 0 in the low half), rounded to nearest
+// even, one v_cvt_pk_bf16_f32 per pair.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, bf16x2v));
+}
+
 // hi + lo bf16 operands of 8 fp32 values (4 of tile 0, then 4 of tile 1)
 __device__ __forceinline__ void split_hilo(const float (&v0)[4], const float (&v1)[4], u4& hi, u4& lo) {
-  uint32_t hb[8], lb[8];
+  const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    hb[r] = float_to_bf16_bits(v0[r]);
-    hb[4 + r] = float_to_bf16_bits(v1[r]);
-    lb[r] = float_to_bf16_bits(v0[r] - bits_to_float(hb[r] << 16));
-    lb[4 + r] = float_to_bf16_bits(v1[r] - bits_to_float(hb[4 + r] << 16));
+  for (int q = 0; q < 4; ++q) {
+    h[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+    l[q] = pack_bf16x2(x[2 * q] - bits_to_float(h[q] << 16), x[2 * q + 1] - bits_to_float(h[q] & 0xffff0000u));
   }
-  hi = (u4){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-  lo = (u4){lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+  hi = (u4){h[0], h[1], h[2], h[3]};
+  lo = (u4){l[0], l[1], l[2], l[3]};
 }
 
 // Map a linear workgroup id to a logical one so that each XCD (ids are dealt
