@@ -801,7 +801,8 @@ __global__ void dustbin_scores_bw(Geom g, const T* Q, const T* K, float* sdr, fl
 constexpr int kSwWaves = 8;
 constexpr int kSwThreads = 64 * kSwWaves;
 
-template <int D, bool COL, int MODE, int RM>
+// RX: the tail depth is exactly RM (a compile-time constant), else any R <= RM.
+template <int D, bool COL, int MODE, int RM, bool RX = false>
 __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(Geom g, BwArgs p) {
   constexpr int RB = D * 2;           // bytes per row (bf16)
   constexpr int CPR = RB / 16;        // 16-byte chunks per row
@@ -841,7 +842,7 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   }
   const size_t L = g.L;
   const size_t BHL = (size_t)nbh * L;
-  const int R = p.R;
+  const int R = RX ? RM : p.R;
   const int TLx = COL ? g.TLc : g.TL;
   const int NT = COL ? g.NTc : g.NT;
   const int NW = NT + kSwWaves - 1;   // window tiles of the block
@@ -1251,12 +1252,13 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     return (size_t)4 * ntens * 32 * D * 2 + (size_t)NWC * 4 * (1 + nv) + 64;  // 4 pair buffers
   };
   if constexpr (kSweep) {
-#define SET_SW(COLV, MODEV, RMV)                                                                        \
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV, RMV>),        \
+#define SET_SW(COLV, MODEV, RMV, RXV)                                                                   \
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV, RMV, RXV>),   \
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds(COLV, MODEV));   \
   if (err != hipSuccess) return err;
-    SET_SW(false, 0, 2) SET_SW(false, 1, 2) SET_SW(true, 0, 2) SET_SW(true, 1, 2) SET_SW(true, 2, 2)
-    SET_SW(false, 1, kMaxR) SET_SW(true, 1, kMaxR)
+    SET_SW(false, 0, 2, false) SET_SW(false, 1, 2, false) SET_SW(true, 0, 2, false) SET_SW(true, 1, 2, false)
+    SET_SW(true, 2, 2, false) SET_SW(false, 1, kMaxR, false) SET_SW(true, 1, kMaxR, false)
+    SET_SW(false, 1, 2, true) SET_SW(true, 1, 2, true)
 #undef SET_SW
   }
   // dV (band) -> add dustbin row, E, vbar^(R).  The bf16 sweep computes E and
@@ -1295,7 +1297,10 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   p.out = f.dQ;
   ps.out = f.dQ;
   if constexpr (kSweep) {
-    if (R <= 2)
+    if (R == 2)  // the tail depth as a compile-time constant
+      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1, 2, true>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st,
+                         g, ps);
+    else if (R < 2)
       hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st, g, ps);
     else
       hipLaunchKernelGGL((bw_sweep_kernel<D, false, 1, kMaxR>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 1), st, g,
@@ -1308,7 +1313,10 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   p.out = f.dK;
   ps.out = f.dK;
   if constexpr (kSweep) {
-    if (R <= 2)
+    if (R == 2)
+      hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1, 2, true>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st,
+                         g, ps);
+    else if (R < 2)
       hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st, g, ps);
     else
       hipLaunchKernelGGL((bw_sweep_kernel<D, true, 1, kMaxR>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 1), st, g,
