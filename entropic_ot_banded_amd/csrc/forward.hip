@@ -849,13 +849,22 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       // u^(t)_i = log2(a_i / rho_i) - c_i - vref (fp64 state), by lane lr = r
       {
         const int rsel = lr & 3;
-        float rsv = rs[0], av = cur.a[0], shv = shift[0];
+        // a_i as opaque registers: selected straight from the array, the
+        // compiler turns the choice into a run-time index and moves the array
+        // to scratch memory (a store and a dependent load in every block)
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ar[r] = cur.a[r];
+          asm volatile("" : "+v"(ar[r]));
+        }
+        float rsv = rs[0], av = ar[0], shv = shift[0];
         bool okv = rowok[0];
 #pragma unroll
         for (int r = 1; r < 4; ++r)
           if (rsel == r) {
             rsv = rs[r];
-            av = cur.a[r];
+            av = ar[r];
             shv = shift[r];
             okv = rowok[r];
           }
