@@ -175,11 +175,21 @@ const char* sinkattn_status_string(int status) {
 
 int sinkattn_timing_enable(int on) {
   TimingState& t = timing();
+  int status = SINKATTN_OK;
+  if (!on) {
+    // release the event pool: no HIP object of the library outlives the
+    // timing session (events still pending are released once they complete)
+    for (hipEvent_t e : t.pool) {
+      const hipError_t r = hipEventDestroy(e);
+      if (r != hipSuccess && status == SINKATTN_OK) status = hip_status(r);
+    }
+    t.pool.clear();
+  }
   t.on = on != 0;
   t.used = 0;
   t.launches.clear();
   t.failed = false;
-  return SINKATTN_OK;
+  return status;
 }
 
 int sinkattn_timing_collect(double* total_ms, long long* launches) {

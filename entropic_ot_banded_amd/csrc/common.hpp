@@ -34,6 +34,20 @@ constexpr int kVmcnt0 = 0x0F70;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// log2(x) of a positive finite fp32 x as fp64, split as x = m 2^e with m in
+// [sqrt(1/2), sqrt(2)): the exponent is exact and the fp32 log is taken of
+// m only, so the absolute error stays near 2^-24 instead of growing with
+// |log2 x| (one fp32 ulp of a potential near -17 is 2^-19).
+__device__ __forceinline__ double log2_split(float x) {
+  int e;
+  float m = frexpf(x, &e);  // m in [1/2, 1)
+  if (m < 0.70710678f) {
+    m *= 2.f;
+    --e;
+  }
+  return (double)e + (double)__builtin_amdgcn_logf(m);
+}
+
 __device__ __forceinline__ float bits_to_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t float_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 

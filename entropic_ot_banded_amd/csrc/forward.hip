@@ -51,6 +51,7 @@ struct IterArgs {
   double* v_out;          // v^(t-1), owners write (nullptr when part_in is nullptr)
   double* v_tail;         // optional copy of v^(t-1)
   double* u_out;          // u^(t), owners write
+  const double* u_prev;   // u^(t-1) (exact column updates), nullptr when t == 1
   double* u_tail;         // optional copy of u^(t)
   float* part_out;        // [BH][nseg][SW] column partials of step t
   float* partd_out;       // [BH][nseg] dustbin-column partials of step t
@@ -209,19 +210,77 @@ __device__ __forceinline__ VIn gather_v(const Geom& g, int bh, int n, int j, con
 // (log2 units, fp64 state; the log of a ratio near 1 is taken in fp32).  The
 // dustbin row adds its entry of P^(t-1,t-2), exp2(s_(delta j) + v^(t-2)_j - M)
 // times a_delta / rho_delta.
-__device__ __forceinline__ double finish_from(const VIn& r, const DustC& dc) {
+// *ok reports whether gamma_j lies in [2^-120, 2^120]; outside that range
+// the result is not usable (see finish_checked).
+__device__ __forceinline__ double finish_from(const VIn& r, const DustC& dc, bool* ok = nullptr) {
   const double vprev = ((r.valid >> kMaxSeg) & 1u) ? r.vprev : 0.0;
   float gam = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxSeg; ++k) gam += ((r.valid >> k) & 1u) ? r.part[k] : 0.f;
   if (dc.on) gam += exp2_fast((float)((double)r.sdr + vprev - dc.m)) * dc.h;
-  return vprev + (double)log2f(r.b / gam);
+  if (ok) *ok = gam >= 0x1p-120f && gam <= 0x1p120f;
+  return vprev + log2_split(r.b * __builtin_amdgcn_rcpf(gam));
 }
 
+// Exact column update of band column j (log2 units, fp64 state):
+//   v_j = log2 b_j - log2 sum_{i in Omega^j} 2^(S2_ij + u_i)
+// with S2_ij = q_i . k_j log2(e) / sqrt(d) recomputed from Q and K, u the
+// row potentials the column update follows (the same step's), and the
+// dustbin row (score sdr_j, potential u_n) when there is one.  The finish
+// takes it when the row pass's weighted column sum gamma_j leaves
+// [2^-120, 2^120]: scores spread so wide that the column's entries underflow
+// against their rows' shifts (the column-side counterpart of the row pass's
+// exact-maximum fallback).  One thread, a plain loop over the column's rows,
+// fp32 scores and an fp64 running log-sum-exp: slow, and reached only for
+// extreme inputs.
+template <typename T, bool COH>
+__device__ double exact_column_v(const Geom& g, int bh, int n, int j, const char* Qb, const char* Kb,
+                                 const double* u, float bj, float sdr_j) {
+  const int D = g.d;
+  const size_t L = g.L;
+  const T* kj = reinterpret_cast<const T*>(Kb) + (size_t)j * D;
+  int i0 = j - g.h2, i1 = j + g.h1;
+  i0 = i0 < 0 ? 0 : i0;
+  i1 = i1 > n - 1 ? n - 1 : i1;
+  double m = -__builtin_inf(), s = 0.0;
+  auto add = [&](double x) {
+    if (x > m) {
+      s = s * exp2(m - x) + 1.0;
+      m = x;
+    } else {
+      s += exp2(x - m);
+    }
+  };
+  for (int i = i0; i <= i1; ++i) {
+    const T* qi = reinterpret_cast<const T*>(Qb) + (size_t)i * D;
+    float acc = 0.f;
+    for (int c = 0; c < D; ++c) acc = __builtin_fmaf(Elt<T>::load(qi, c), Elt<T>::load(kj, c), acc);
+    add((double)(acc * g.scale2) + ld_shared<COH>(u + bh * L + i));
+  }
+  if (g.dustbin) add((double)sdr_j + ld_shared<COH>(u + bh * L + n));
+  return log2((double)bj) - m - log2(s);
+}
+
+// v^(t-1)_j from the gathered inputs, or from its exact column log-sum-exp
+// when gamma_j is out of range (u_prev: u^(t-1); Qb, Kb: the (b, h) slices).
+template <typename T, bool COH>
+__device__ __forceinline__ double finish_checked(const Geom& g, const VIn& r, const DustC& dc, int bh, int n, int j,
+                                                 const char* Qb, const char* Kb, const double* u_prev) {
+  bool ok;
+  const double v = finish_from(r, dc, &ok);
+  if (ok || !u_prev) return v;
+  return exact_column_v<T, COH>(g, bh, n, j, Qb, Kb, u_prev, r.b, r.sdr);
+}
+
+template <typename T>
 __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, const double* v_prev2,
                                            const float* part_in, const float* b, int bb,
-                                           const double* dstate, const float* sdr) {
-  return finish_from(gather_v(g, bh, n, j, v_prev2, part_in, b, bb, sdr), load_dust(g, bh, dstate));
+                                           const double* dstate, const float* sdr, const void* Q, const void* K,
+                                           const double* u) {
+  const size_t slice = (size_t)bh * g.L * g.d * sizeof(T);
+  return finish_checked<T, false>(g, gather_v(g, bh, n, j, v_prev2, part_in, b, bb, sdr), load_dust(g, bh, dstate),
+                                  bh, n, j, reinterpret_cast<const char*>(Q) + slice,
+                                  reinterpret_cast<const char*>(K) + slice, u);
 }
 
 // Steps t_begin .. t_end of one persistent launch (see iter_kernel): the
@@ -233,7 +292,7 @@ __device__ __forceinline__ double finish_v(const Geom& g, int bh, int n, int j, 
 struct StepPlan {
   float* part;       // [2][part_slot] column partials (by step parity)
   double* vbuf;      // [2][BHL] v ping-pong
-  double* ubuf;      // [BHL] latest u
+  double* ubuf;      // [2][BHL] u^(t) in slot t & 1
   double* tail_u;    // [R + 1][BHL]
   double* tail_v;    // [R + 1][BHL]
   size_t part_slot, BHL;
@@ -251,7 +310,8 @@ __device__ __forceinline__ IterArgs step_args(const IterArgs& base, const StepPl
   a.v_prev2 = t <= 2 ? nullptr : q.vbuf + (size_t)((t - 2) & 1) * q.BHL;
   a.v_out = t == 1 ? nullptr : q.vbuf + (size_t)((t - 1) & 1) * q.BHL;
   a.v_tail = (t >= 2 && t - 1 >= q.T) ? q.tail_v + (size_t)(t - 1 - q.T) * q.BHL : nullptr;
-  a.u_out = q.ubuf;
+  a.u_out = q.ubuf + (size_t)(t & 1) * q.BHL;
+  a.u_prev = t >= 2 ? q.ubuf + (size_t)((t - 1) & 1) * q.BHL : nullptr;
   a.u_tail = t >= q.T ? q.tail_u + (size_t)(t - q.T) * q.BHL : nullptr;
   a.part_out = q.part + (size_t)(t & 1) * q.part_slot;
   a.partd_out = nullptr;
@@ -331,6 +391,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     double* v_out;
     double* v_tail;
     double* u_tail;
+    double* u_out;
+    const double* u_prev;
     float* part_out;
     int first;
   };
@@ -343,6 +405,8 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       sptr.v_out = a.v_out;
       sptr.v_tail = a.v_tail;
       sptr.u_tail = a.u_tail;
+      sptr.u_out = a.u_out;
+      sptr.u_prev = a.u_prev;
       sptr.part_out = a.part_out;
       sptr.first = a.first;
     }
@@ -364,8 +428,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     else return p0.v_tail;
   };
   auto s_u_out = [&]() -> double* {
-    if constexpr (PERS) return q.ubuf;
+    if constexpr (PERS) return sptr.u_out;
     else return p0.u_out;
+  };
+  auto s_u_prev = [&]() -> const double* {
+    if constexpr (PERS) return sptr.u_prev;
+    else return p0.u_prev;
   };
   auto s_u_tail = [&]() -> double* {
     if constexpr (PERS) return sptr.u_tail;
@@ -458,7 +526,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     if (tid < NWC) {
       float w = kNegInf;
       if (colok) {
-        const double vj = s_part_in() ? finish_from(pin, dc) : 0.0;
+        const double vj = s_part_in() ? finish_checked<T, PERS>(g, pin, dc, bh, n, jc, Qb, Kb, s_u_prev()) : 0.0;
         publish_v(jc, vj);
         w = (float)(vj - vref);
       }
@@ -870,8 +938,10 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           }
         if (lr < 4 && okv) {
           const int i = i0 + 4 * lg + rsel;
-          const double u = (double)log2f(av / rsv) - (double)shv - vref;
-          s_u_out()[bh * L + i] = u;
+          const double u = log2_split(av * __builtin_amdgcn_rcpf(rsv)) - (double)shv - vref;
+          // device scope in the persistent launch: an exact column update of
+          // another workgroup may read it in the next step
+          st_shared<PERS>(s_u_out() + bh * L + i, u);
           if (s_u_tail()) gmem(s_u_tail())[bh * L + i] = u;
         }
       }
@@ -917,8 +987,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     // and 3, which finish their strips first; block k + 1 overwrites that
     // buffer only after the barrier)
     if (bi > 0 && (wave == 2 || wave == 3)) fold(k - DIR, buf ^ 1, rbp, false, DIR > 0, 2 * 64);
-    if constexpr (PERS)  // the region's last fold: its stores complete before the barrier
-      if (bi == bi_head - 1 && (wave == 2 || wave == 3)) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    // the region's last fold: its stores complete before the barrier, and so
+    // do every wave's u stores of the region's rows (a neighbour's exact
+    // column update may read them once head(t) is out)
+    if constexpr (PERS)
+      if (bi == bi_head - 1) __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
     // ---- v^(t-1) of the columns entering with block k + 1 (written to
     // memory during the next strip: a store still in flight at the loop top
@@ -927,7 +1000,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
     if (more && ec >= 0) {
       const int j = jn0 + ec;
       if (j >= 0 && j < n) {
-        const double vj = s_part_in() ? finish_from(vin, dc) : 0.0;
+        const double vj = s_part_in() ? finish_checked<T, PERS>(g, vin, dc, bh, n, j, Qb, Kb, s_u_prev()) : 0.0;
         jpend = j;
         vpend = vj;
         wnew = (float)(vj - vref);
@@ -1010,6 +1083,9 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         wait_for(q.head, e_idx, has_e, t - 1, q.done, right ? me - 1 : me + 1, far_now && (right ? has_l : has_r),
                  t - 1);
     }
+    // every wave's u^(t-1) stores have completed (they drained during the
+    // neighbour wait): the window's exact column updates may read them
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     vref = s_v_prev2() ? ld_shared<true>(s_v_prev2() + bh * L + seg_r0) : 0.0;
     {
@@ -1027,7 +1103,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       if (tid < NWC) {
         float w = kNegInf;
         if (colok) {
-          const double vj = s_part_in() ? finish_from(pin, dc) : 0.0;
+          const double vj = s_part_in() ? finish_checked<T, true>(g, pin, dc, bh, n, jc, Qb, Kb, s_u_prev()) : 0.0;
           publish_v(jc, vj);
           w = (float)(vj - vref);
         }
@@ -1058,6 +1134,7 @@ struct DustArgs {
   const float* partd;   // [BH][nseg] dustbin-column partials of step t
   double* dstate;       // in: state after t-1 (ignored when first); out: after t
   const float* sdr;
+  const float* sdc;     // dustbin column scores (exact column update)
   double* u_tail;       // optional: u^(t) slot
   double* v_tail;       // optional: v^(t) slot
   double* u_out;        // latest-u buffer (dustbin entry)
@@ -1100,16 +1177,52 @@ __global__ __launch_bounds__(256) void dustbin_step(Geom g, DustArgs p) {
     if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
+  __shared__ double sh_ud;
+  __shared__ int sh_exact;
+  const float bd = p.b[(size_t)bb * L + n];
+  double vd = 0.0;
   if (tid == 0) {
     const float rho = red[0];
     const float ad = p.a[(size_t)bb * L + n];
-    const float bd = p.b[(size_t)bb * L + n];
     const double ud = log2((double)ad) - log2((double)rho) - M;
     const float hd = ad / rho;
     float gam = 0.f;
     for (int sg = 0; sg < g.nseg && sg * g.SB * kBlockRows < n; ++sg) gam += p.partd[(size_t)bh * g.nseg + sg];
     gam += exp2_fast((float)((double)srow[n] + vd_prev - M)) * hd;  // corner of P^(t,t-1)
-    const double vd = vd_prev + log2((double)bd) - log2((double)gam);
+    vd = vd_prev + log2((double)bd) - log2((double)gam);
+    sh_ud = ud;
+    sh_exact = !(gam >= 0x1p-120f && gam <= 0x1p120f);
+  }
+  __syncthreads();
+  if (sh_exact) {
+    // gamma out of range: the exact column log-sum-exp of the dustbin column,
+    // log2 sum_i 2^(S2_i,delta + u^(t)_i) over the real rows and the corner
+    const double ud = sh_ud;
+    const float* scol = p.sdc + bh * L;
+    double mx = -__builtin_inf();
+    for (int i = tid; i < n; i += blockDim.x) mx = fmax(mx, (double)scol[i] + p.u_out[bh * L + i]);
+    redd[tid] = mx;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) redd[tid] = fmax(redd[tid], redd[tid + s]);
+      __syncthreads();
+    }
+    const double Mc = fmax(redd[0], (double)srow[n] + ud);
+    __syncthreads();
+    double sc = 0.0;
+    for (int i = tid; i < n; i += blockDim.x) sc += exp2((double)scol[i] + p.u_out[bh * L + i] - Mc);
+    redd[tid] = sc;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) redd[tid] += redd[tid + s];
+      __syncthreads();
+    }
+    if (tid == 0) vd = log2((double)bd) - Mc - log2(redd[0] + exp2((double)srow[n] + ud - Mc));
+  }
+  if (tid == 0) {
+    const double ud = sh_ud;
+    const float rho = red[0];
+    const float hd = p.a[(size_t)bb * L + n] / rho;
     double* ds = p.dstate + 4 * bh;
     ds[0] = ud;
     ds[1] = vd;
@@ -1162,12 +1275,12 @@ __global__ void zero_start(Geom g, double* tail_u0, double* tail_v0) {
 // row update of the next step.  So
 //   e_t = sum_i |rowsum_i(P^(t,t)) - a_i| = sum_i a_i |2^(u^(t)_i - u^(t+1)_i) - 1|
 // over the active rows (the dustbin row included), in fp64 and a fixed order.
-// The step carrying the check left u^(t+1) in `unew` and the latest-u buffer
-// untouched; this kernel also moves the potentials on: u^(t) to `uold_copy`
-// (the stopped-base slot, should the check pass) and u^(t+1) to the latest-u
-// buffer.  One workgroup per (b, h).
-__global__ __launch_bounds__(256) void base_check(Geom g, const float* a, double* ubuf, const double* unew,
-                                                  double* uold_copy, double* err) {
+// The step carrying the check left u^(t+1) in `unew` and u^(t) in its
+// parity slot `uold`; this kernel also moves the potentials on: u^(t) to
+// `uold_copy` (the stopped-base slot, should the check pass) and u^(t+1) to
+// its parity slot `unext`.  One workgroup per (b, h).
+__global__ __launch_bounds__(256) void base_check(Geom g, const float* a, const double* uold, double* unext,
+                                                  const double* unew, double* uold_copy, double* err) {
   const int bh = blockIdx.x;
   const int bb = bh / g.H;
   const int n = real_len(g, bb);
@@ -1178,10 +1291,10 @@ __global__ __launch_bounds__(256) void base_check(Geom g, const float* a, double
   double acc = 0.0;
   for (int i = tid; i <= last; i += 256) {
     const size_t o = (size_t)bh * L + i;
-    const double uo = ubuf[o], un = unew[o];
+    const double uo = uold[o], un = unew[o];
     acc += (double)a[(size_t)bb * L + i] * fabs(expm1((uo - un) * 0.6931471805599453));
     uold_copy[o] = uo;
-    ubuf[o] = un;
+    unext[o] = un;
   }
   red[tid] = acc;
   __syncthreads();
@@ -1263,7 +1376,8 @@ __global__ __launch_bounds__(512) void output_kernel(Geom g, OutArgs p) {
   if (r0 >= n) return;
 
   if (tid == 0)
-    sh_vref = p.part_in ? finish_v(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr) : 0.0;
+    sh_vref = p.part_in ? finish_v<T>(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr, p.Q, p.K, p.u_in)
+                        : 0.0;
   __syncthreads();
   const double vref = sh_vref;
 
@@ -1274,7 +1388,7 @@ __global__ __launch_bounds__(512) void output_kernel(Geom g, OutArgs p) {
     float w = kNegInf;
     if (j >= 0 && j < n) {
       double vj = 0.0;
-      if (p.part_in) vj = finish_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
+      if (p.part_in) vj = finish_v<T>(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr, p.Q, p.K, p.u_in);
       if (j >= r0 && j < r0 + kBlockRows) {
         p.v_out[bh * L + j] = (float)(vj * ln2);
         if (p.v_tail) p.v_tail[bh * L + j] = vj;
@@ -1490,7 +1604,9 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
   float* wv = reinterpret_cast<float*>(smem + NBUF * 2 * TBYTES);  // [NWC] v_j - vref
 
   if (tid == 0)
-    sh_vref = p.part_in ? finish_v(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr) : 0.0;
+    sh_vref = p.part_in ? finish_v<bf16_t>(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr, p.Q, p.K,
+                                           p.u_in)
+                        : 0.0;
   __syncthreads();
   const double vref = sh_vref;
   for (int c = tid; c < NWC; c += kThreads) {
@@ -1498,7 +1614,8 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
     float w = kNegInf;
     if (j >= 0 && j < n) {
       double vj = 0.0;
-      if (p.part_in) vj = finish_v(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr);
+      if (p.part_in)
+        vj = finish_v<bf16_t>(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr, p.Q, p.K, p.u_in);
       if (j >= r0 && j < r0 + kBlockRows) {
         p.v_out[bh * L + j] = (float)(vj * ln2);
         if (p.v_tail) p.v_tail[bh * L + j] = vj;
@@ -1773,7 +1890,8 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     a.v_prev2 = (t <= 2) ? nullptr : w.vbuf + (size_t)((t - 2) & 1) * BHL;
     a.v_out = (t == 1) ? nullptr : w.vbuf + (size_t)((t - 1) & 1) * BHL;
     a.v_tail = (t >= 2 && t - 1 >= Tbase) ? w.tail_v + (size_t)(t - 1 - Tbase) * BHL : nullptr;
-    a.u_out = w.ubuf;
+    a.u_out = w.ubuf + (size_t)(t & 1) * BHL;
+    a.u_prev = t >= 2 ? w.ubuf + (size_t)((t - 1) & 1) * BHL : nullptr;
     a.u_tail = (t >= Tbase) ? w.tail_u + (size_t)(t - Tbase) * BHL : nullptr;
     if (check) {
       a.v_tail = w.tail_v;
@@ -1812,6 +1930,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       da.partd = a.partd_out;
       da.dstate = w.dstate;
       da.sdr = w.sdr;
+      da.sdc = w.sdc;
       da.u_tail = a.u_tail;
       da.v_tail = (t >= Tbase) ? w.tail_v + (size_t)(t - Tbase) * BHL : nullptr;
       da.u_out = a.u_out;
@@ -1877,8 +1996,8 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       const bool check = c >= 1 && c % f.stop.every == 0 && c + 2 <= f.T;
       launch_step(t, f.T, check);
       if (!check) continue;
-      hipLaunchKernelGGL(base_check, dim3(nbh), dim3(256), 0, st, g, f.a, w.ubuf, w.tail_u + BHL, w.tail_u,
-                         w.err);
+      hipLaunchKernelGGL(base_check, dim3(nbh), dim3(256), 0, st, g, f.a, w.ubuf + (size_t)(c & 1) * BHL,
+                         w.ubuf + (size_t)(t & 1) * BHL, w.tail_u + BHL, w.tail_u, w.err);
       err = hipMemcpyAsync(eh.data(), w.err, (size_t)nbh * sizeof(double), hipMemcpyDeviceToHost, st);
       if (err == hipSuccess) err = hipStreamSynchronize(st);
       if (err != hipSuccess) return err;
@@ -1909,7 +2028,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   o.b = f.b;
   o.part_in = (Nrun == 0) ? nullptr : w.part + (size_t)(Nrun & 1) * part_slot;
   o.v_prev2 = (Nrun <= 1) ? nullptr : w.vbuf + (size_t)((Nrun - 1) & 1) * BHL;
-  o.u_in = (Nrun == 0) ? nullptr : w.ubuf;
+  o.u_in = (Nrun == 0) ? nullptr : w.ubuf + (size_t)(Nrun & 1) * BHL;
   o.dstate = (g.dustbin && Nrun >= 1) ? w.dstate : nullptr;
   o.sdr = w.sdr;
   o.sdc = w.sdc;

@@ -53,7 +53,7 @@ __device__ inline int real_len(const Geom& g, int bb) {
 struct Workspace {
   double* tail_u;  // [R+1][BHL] u^(0..R)
   double* tail_v;  // [R+1][BHL] v^(0..R)
-  double* ubuf;    // [BHL]    latest u
+  double* ubuf;    // [2][BHL] u^(t) by step parity (slot t & 1)
   double* vbuf;    // [2][BHL] ping-pong v
   double* dstate;  // [BH][4]  dustbin (u, v, row shift, h)
   float* part;     // [2][BH][nseg][SW] column partial sums
@@ -81,7 +81,7 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   auto take_d = [&](size_t n) { return reinterpret_cast<double*>(take(2 * n)); };
   w.tail_u = take_d((size_t)(R + 1) * BHL);
   w.tail_v = take_d((size_t)(R + 1) * BHL);
-  w.ubuf = take_d(BHL);
+  w.ubuf = take_d(2 * BHL);
   w.vbuf = take_d(2 * BHL);
   w.dstate = take_d(4 * BH);
   w.part = take(2 * BH * (size_t)g.nseg * g.SW);

@@ -225,8 +225,10 @@ int sinkattn_block_contraction(const void *Q, const void *K, int W, const sinkat
  * events, writes the summed bracketed time in milliseconds and the number of
  * Sinkhorn steps it covers since the previous collect (or enable), and resets
  * the counters.  Process-wide state, not thread-safe; events are created
- * lazily and reused.  Returns SINKATTN_OK, SINKATTN_EINVAL (NULL outputs) or
- * SINKATTN_EHIP. */
+ * lazily, reused while timing stays on, and destroyed by
+ * sinkattn_timing_enable(0) (call it before the HIP runtime shuts down, so
+ * that no library-owned HIP object outlives it).  Returns SINKATTN_OK,
+ * SINKATTN_EINVAL (NULL outputs) or SINKATTN_EHIP. */
 int sinkattn_timing_enable(int on);
 int sinkattn_timing_collect(double *total_ms, long long *steps);
 

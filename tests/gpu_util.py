@@ -140,9 +140,48 @@ def run_oracle(prob: workloads.Problem, T=None, R=None, W=None, backward=True, p
                                 prob.dustbin, processes=processes)
 
 
+# Parity bounds.  Normwise relative error ||x - x*|| / ||x*|| over active
+# entries (the tolerance the benchmark spec states: 1e-5 on O, u, v and 1e-4 on dQ,
+# dK, dV for fp32 inputs; the bf16 bounds follow from P and dS entering the
+# bf16 MFMAs as hi + lo pairs, about 16 mantissa bits), and element-wise
+# max|x - x*| / max|x*| ("<key>_max"), which an error confined to a few rows
+# (band ends, ragged tails, the dustbin row) cannot hide in.
+TOL_F32 = {"O": 1e-5, "u": 1e-5, "v": 1e-5, "uv_gauge": 1e-5, "dQ": 1e-4, "dK": 1e-4, "dV": 1e-4,
+           "O_max": 4e-5, "u_max": 2e-5, "v_max": 4e-5, "dQ_max": 4e-4, "dK_max": 4e-4, "dV_max": 4e-4}
+TOL_BF16 = {"O": 1e-4, "u": 1e-4, "v": 1e-4, "uv_gauge": 1e-4, "dQ": 1e-3, "dK": 1e-3, "dV": 1e-3,
+            "O_max": 4e-4, "u_max": 2e-4, "v_max": 4e-4, "dQ_max": 4e-3, "dK_max": 4e-3, "dV_max": 4e-3}
+# v is held to its own per-tensor bound unless ||v*|| < V_SMALL * ||u*||:
+# then v is a small remainder of the potential pair (uniform marginals put
+# the scale in u), its relative error measures only the absolute rounding of
+# the pair, and it is bounded against the pair's scale instead (v_pair).
+V_SMALL = 0.1
+
+
+def max_rel_err(x, ref, mask=None, scale=None):
+    """Element-wise max|x - ref| / max|ref| over finite reference entries
+    (and `mask`); `scale` replaces max|ref| when given."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    fin = np.isfinite(ref)
+    if mask is not None:
+        fin &= mask
+    if not fin.any():
+        return 0.0
+    bad = np.isfinite(x) != np.isfinite(ref)
+    if mask is not None:
+        bad &= mask
+    if bad.any():
+        return np.inf
+    den = np.abs(ref[fin]).max() if scale is None else scale
+    return float(np.abs(x[fin] - ref[fin]).max() / (den if den > 0 else 1.0))
+
+
 def compare(gpu, ref, prob, keys=("O", "u", "v", "dQ", "dK", "dV")):
-    """Relative errors per output over active tokens, plus the gauge-removed
-    potential pair (O and the plans are invariant under u + c, v - c)."""
+    """Relative errors per output over active tokens: normwise (key) and
+    element-wise ("<key>_max"); for v also the pair-scaled errors ("v_pair",
+    "v_pair_max") and the ratio ||v*|| / ||u*|| ("vu_ratio"); plus the
+    gauge-removed potential pair (O and the plans are invariant under
+    u + c, v - c)."""
     act = active_mask(prob)
     act_bhl = np.broadcast_to(act[:, None, :], gpu["u"].shape)
     act_rows = np.broadcast_to(act[:, None, :, None], gpu["O"].shape)
@@ -150,19 +189,21 @@ def compare(gpu, ref, prob, keys=("O", "u", "v", "dQ", "dK", "dV")):
     for k in keys:
         if k not in gpu:
             continue
-        if k == "u":
+        if k in ("u", "v"):
             errs[k] = rel_err(gpu[k], ref[k], act_bhl)
-        elif k == "v":
-            # v alone can vanish (wide bands, symmetric problems: v ~ 0 with
-            # u ~ 2 log(1/L)); its error is measured against the scale of the
-            # potential pair, max(||v||, ||u||), and the strict per-tensor
-            # ratio is reported as v_strict.
-            errs["v_strict"] = rel_err(gpu[k], ref[k], act_bhl)
-            nv = np.linalg.norm(np.asarray(ref["v"], np.float64)[act_bhl])
-            nu = np.linalg.norm(np.asarray(ref["u"], np.float64)[act_bhl])
-            errs[k] = errs["v_strict"] * nv / max(nv, nu) if nv > 0 else errs["v_strict"]
+            errs[k + "_max"] = max_rel_err(gpu[k], ref[k], act_bhl)
+            if k == "v":
+                rv = np.asarray(ref["v"], np.float64)[act_bhl]
+                ru = np.asarray(ref["u"], np.float64)[act_bhl]
+                nv, nu = np.linalg.norm(rv), np.linalg.norm(ru)
+                errs["vu_ratio"] = float(nv / nu) if nu > 0 else np.inf
+                errs["v_pair"] = errs["v"] * nv / max(nv, nu) if nv > 0 else errs["v"]
+                mv = np.abs(rv).max() if rv.size else 0.0
+                mu = np.abs(ru).max() if ru.size else 0.0
+                errs["v_pair_max"] = max_rel_err(gpu[k], ref[k], act_bhl, scale=max(mv, mu))
         else:
             errs[k] = rel_err(gpu[k], ref[k], act_rows)
+            errs[k + "_max"] = max_rel_err(gpu[k], ref[k], act_rows)
             # filler rows must be exactly zero
             if (~act_rows).any():
                 assert np.all(gpu[k][~act_rows] == 0), f"{k}: nonzero filler rows"
@@ -177,6 +218,33 @@ def compare(gpu, ref, prob, keys=("O", "u", "v", "dQ", "dK", "dV")):
         # inactive potentials are -inf
         assert np.all(np.isneginf(gpu["u"][~act_bhl])) and np.all(np.isneginf(gpu["v"][~act_bhl]))
     return errs
+
+
+def parity_failures(errs, tol, skip=()):
+    """The bounds `errs` violates, as messages.  v takes its own bound when
+    ||v*|| >= V_SMALL ||u*||, the pair-scaled one (v_pair, v_pair_max) when v
+    is a small remainder of the pair."""
+    bad = []
+    small_v = errs.get("vu_ratio", np.inf) < V_SMALL
+    for k, lim in tol.items():
+        if k in skip or k not in errs:
+            continue
+        val = errs[k]
+        if small_v and k in ("v", "v_max"):
+            val = errs["v_pair" if k == "v" else "v_pair_max"]
+            k = f"{k} (pair-scaled: ||v*|| / ||u*|| = {errs['vu_ratio']:.3f} < {V_SMALL})"
+        if not (val <= lim):
+            bad.append(f"{k}: {val:.3e} > {lim:.1e}")
+    return bad
+
+
+def assert_parity(errs, tol, label="", skip=()):
+    bad = parity_failures(errs, tol, skip)
+    assert not bad, f"{label}: " + "; ".join(bad)
+
+
+def fmt_errs(errs):
+    return {k: f"{v:.2e}" for k, v in errs.items()}
 
 
 def log(*a):

@@ -24,14 +24,10 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import compare, log, run_gpu, run_gpu_converge, run_oracle
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_parity, compare, fmt_errs, log, run_gpu,
+                            run_gpu_converge, run_oracle)
 
 pytestmark = pytest.mark.gpu
-
-TOL_F32 = {"O": 1e-5, "u": 1e-5, "v": 1e-5, "uv_gauge": 1e-5, "v_strict": float("inf"),
-           "dQ": 1e-4, "dK": 1e-4, "dV": 1e-4}
-TOL_BF16 = {"O": 1e-4, "u": 1e-4, "v": 1e-4, "uv_gauge": 1e-4, "v_strict": float("inf"),
-            "dQ": 1e-3, "dK": 1e-3, "dV": 1e-3}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -77,9 +73,8 @@ def test_converged_base_matches_oracle(name, mk, every, idx, tols):
     assert abs(gpu["err_last"] - e_star) <= 1e-2 * e_star, (gpu["err_last"], e_star)
     ref = run_oracle(prob, T=c_star)
     errs = compare(gpu, ref, prob)
-    log("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
-    for k, v in errs.items():
-        assert v <= tols[k], f"{name}: {k} rel err {v:.3e} > {tols[k]:.1e}"
+    log("   errors:", fmt_errs(errs))
+    assert_parity(errs, tols, name)
 
 
 @pytest.mark.parametrize("tol_kind", ["never", "first"])

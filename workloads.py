@@ -124,14 +124,38 @@ def _uniform_marginals(B, L, n_real, dustbin=False, dustbin_mass=0.1):
     return a, a.copy()
 
 
+def _random_marginals(rng, B, L, n_real, sigma, dustbin=False, dustbin_mass=0.1):
+    """Marginals proportional to exp(N(0, sigma^2)) on the real tokens,
+    normalised to 1 (to 1 - dustbin_mass with a dustbin, which keeps its
+    mass); a and b drawn independently, a first."""
+    out = []
+    for _ in range(2):
+        m = np.zeros((B, L), dtype=np.float64)
+        for bi in range(B):
+            n = int(n_real[bi])
+            if n == 0:
+                if dustbin:
+                    m[bi, 0] = 1.0
+                continue
+            w = np.exp(rng.standard_normal(n) * sigma)
+            real = (1.0 - dustbin_mass) if dustbin else 1.0
+            m[bi, :n] = real * w / w.sum()
+            if dustbin:
+                m[bi, n] = dustbin_mass
+        out.append(m.astype(np.float32))
+    return out[0], out[1]
+
+
 def custom(B=1, H=1, L=64, d=16, W=17, T=20, R=2, dtype="f32", seed=0,
            scale=None, lengths=None, dustbin=False, dustbin_mass=0.1,
-           filler="zero", name="custom") -> Problem:
+           filler="zero", marginals_sigma=None, name="custom") -> Problem:
     """A generic seeded problem: Q, K, V ~ N(0, scale^2), dO ~ N(0, 1).
 
     scale defaults to 1/sqrt(d).  lengths (list/array of B ints) makes the
     batch ragged; positions >= lengths[b] (+1 with a dustbin) are filler and
-    are zeroed (filler="zero") or left random (filler="random").
+    are zeroed (filler="zero") or left random (filler="random").  Marginals
+    are uniform over the real tokens, or, with marginals_sigma, drawn after
+    dO as exp(N(0, sigma^2)) weights normalised per sequence.
     """
     rng = np.random.default_rng(seed)
     if scale is None:
@@ -151,7 +175,10 @@ def custom(B=1, H=1, L=64, d=16, W=17, T=20, R=2, dtype="f32", seed=0,
             first_filler = int(n_real[bi]) + (1 if dustbin else 0)
             for X in (Q, K, V):
                 X[bi, :, first_filler:, :] = 0.0
-    a, b = _uniform_marginals(B, L, n_real, dustbin, dustbin_mass)
+    if marginals_sigma is None:
+        a, b = _uniform_marginals(B, L, n_real, dustbin, dustbin_mass)
+    else:
+        a, b = _random_marginals(rng, B, L, n_real, marginals_sigma, dustbin, dustbin_mass)
     return Problem(name, _finish(Q, dtype), _finish(K, dtype), _finish(V, dtype),
                    _finish(dO, dtype), a, b, W, T, R, dtype, lengths, dustbin)
 
