@@ -9,8 +9,11 @@ bf16 (seeded synthetic data); fp32 accumulation, fp64 Sinkhorn state.
 One step = sinkattn_forward + sinkattn_backward over the whole batch (every
 row of the hot path), inputs resident in HBM.  Prints ONE JSON line with the
 throughput, the roofline of the dominant kernel (the fused Sinkhorn step,
-timed per launch with HIP events on its stream) and the float64 oracle timed
-on the host's cores on a bounded sample of the same workload.
+timed per launch with HIP events on its stream, against the MFMA/exp peak
+with the work counted per half-step: 4 d flops and 2 exps per band entry
+per Sinkhorn step), the same workload with the R = 4 tail, the other
+workloads' step times, and the float64 oracle timed on the host's cores on a
+bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--R 2] [--no-cpu-baseline]
 
@@ -141,7 +144,8 @@ def load_pmc(launch_units=None):
     return (fetch + write) * 1024.0
 
 
-PROF_ARGS = "--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0 --no-peaks"
+PROF_ARGS = ("--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0 --no-peaks "
+             "--r4-steps 0 --no-other-configs")
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $REPO/gpurun_out/prof/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
              + PROF_ARGS)
@@ -278,34 +282,79 @@ def summarize_sq(d):
     print("\n".join(lines))
 
 
-def cpu_baseline(prob, heads, length=None):
+def host_cores() -> int:
+    """CPU cores this process may use (the scheduler's affinity set)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(prob, heads=None, length=None):
     """The float64 oracle (as is) on a bounded sample of the same workload:
-    `heads` of its H independent heads (same input values), all L tokens
-    unless `length` cuts a prefix (then with uniform marginals over the
-    prefix), one process; scaled to whole-workload tokens/s (the work is
-    linear in L and in H)."""
+    `heads` of its H independent heads (same input values; default one per
+    host core, at most H), all L tokens unless `length` cuts a prefix (then
+    with uniform marginals over the prefix), one process per head; scaled to
+    whole-workload tokens/s (the work is linear in L and in H)."""
     import numpy as np
 
     import oracle
     import workloads
 
+    cores = host_cores()
+    if heads is None:
+        heads = max(1, min(prob.H, cores, 16))
+    procs = min(heads, cores)
     sub = workloads.make(5, heads=list(range(heads)), R=prob.R)
     Ls = sub.L if length is None else min(length, sub.L)
     sl = lambda x: np.ascontiguousarray(x[:, :, :Ls])
     a = np.full((sub.B, Ls), 1.0 / Ls, dtype=np.float32)
     t0 = time.perf_counter()
     oracle.forward_backward_batch(sl(sub.Q), sl(sub.K), sl(sub.V), a, a.copy(), sub.W, sub.T, sub.R,
-                                  sl(sub.dO), processes=1)
+                                  sl(sub.dO), processes=procs)
     dt = time.perf_counter() - t0
     # the metric counts a token once for all H heads: the whole workload
     # (B L tokens, H heads) takes dt * (H / heads) * (L / Ls)
     value = prob.B * prob.L / (dt * (prob.H / heads) * (prob.L / Ls))
-    return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": procs, "kind": "oracle",
             "sample": f"first {Ls} of {prob.L} tokens of {heads} of {prob.H} heads (independent problems) "
                       f"of the same inputs, uniform marginals over the sample, full T={sub.T}, R={sub.R}, "
-                      f"forward+backward, float64 numpy/scipy, 1 process: {dt:.1f} s; "
-                      f"scaled to the whole workload (work is linear in L and in H)",
+                      f"forward+backward, float64 numpy/scipy, {procs} processes (one head each) on "
+                      f"{cores} host cores: {dt:.1f} s; scaled to the whole workload (work is linear in L and in H)",
             "seconds": dt}
+
+
+def time_workload(eoba, torch, prob, steps, warmup, dev, tensors=None):
+    """Mean ms of one forward + backward of `prob` (inputs resident on the
+    device; `tensors` = (Q, K, V, dO) already there), HIP events on the
+    current stream around `steps` back-to-back steps after `warmup` untimed
+    ones."""
+    import numpy as np
+
+    dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt).contiguous()  # noqa: E731
+    Q, K, V, dO = tensors if tensors is not None else (up(prob.Q), up(prob.K), up(prob.V), up(prob.dO))
+    a = torch.from_numpy(prob.a).to(dev)
+    b = torch.from_numpy(prob.b).to(dev)
+    ln = None if prob.lengths is None else torch.from_numpy(prob.lengths.astype(np.int32)).to(dev)
+    ws = None
+
+    def step():
+        nonlocal ws
+        O, _, _, ws = eoba.forward(Q, K, V, prob.W, prob.T, prob.R, a, b, ln, prob.dustbin, workspace=ws)
+        eoba.backward(Q, K, V, prob.W, prob.T, prob.R, a, b, O, dO, ws, ln, prob.dustbin)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps
 
 
 def main():
@@ -328,6 +377,10 @@ def main():
     ap.add_argument("--certificate-tau", type=float, default=1e-5)
     ap.add_argument("--contraction-block", type=int, default=128,
                     help="also time the projective contraction diagnostic at this block size (0: skip)")
+    ap.add_argument("--r4-steps", type=int, default=5,
+                    help="also time the same workload with the R=4 tail over this many steps (0: skip)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the step times of the tiny, mid, protein-like and dustbin workloads")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
@@ -373,12 +426,26 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # forward / backward split: events between the launches of every timed
+    # step, on the same stream (the host enqueues ahead, so the stream runs
+    # back to back and each bracket is device time)
+    fb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step_split(e3):
+        nonlocal ws
+        e3[0].record(stream)
+        O, u, v, ws = eoba.forward(Q, K, V, W, T, R, a, b, workspace=ws)
+        e3[1].record(stream)
+        dQ, dK, dV, _ = eoba.backward(Q, K, V, W, T, R, a, b, O, dO, ws)
+        e3[2].record(stream)
+        return O, dQ
+
     eoba.timing_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
-    for _ in range(args.steps):
-        O, dQ = step()
+    for i in range(args.steps):
+        O, dQ = step_split(fb[i])
     ev[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -387,16 +454,8 @@ def main():
     eoba.timing_enable(False)
     if not (torch.isfinite(O).all() and torch.isfinite(dQ).all()):
         raise RuntimeError("non-finite output")
-
-    # separate forward / backward split (untimed region for the main value)
-    fb = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    fb[0].record(stream)
-    O, u, v, ws = eoba.forward(Q, K, V, W, T, R, a, b, workspace=ws)
-    fb[1].record(stream)
-    eoba.backward(Q, K, V, W, T, R, a, b, O, dO, ws)
-    fb[2].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms, bwd_ms = fb[0].elapsed_time(fb[1]), fb[1].elapsed_time(fb[2])
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in fb) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in fb) / args.steps
 
     # The convergence-controlled base on the same inputs, T as its cap
     # (sinkattn_forward_converge; host-timed, since it waits at each check).
@@ -427,15 +486,15 @@ def main():
     if args.certificate_rmax > 0:
         Rm = args.certificate_rmax
         Oc, _, _, wsc = eoba.forward(Q, K, V, W, T, Rm, a, b)
-        eoba.tail_certificate(Q, K, V, W, T, Rm, a, b, Oc, dO, wsc)  # warm
+        eoba.tail_certificate(Q, K, V, W, T, Rm, a, b, Oc, dO, wsc, tau=args.certificate_tau)  # warm
         torch.cuda.synchronize()
         c0 = time.perf_counter()
-        _, _, _, eta = eoba.tail_certificate(Q, K, V, W, T, Rm, a, b, Oc, dO, wsc)
+        _, _, _, eta, r_sel = eoba.tail_certificate(Q, K, V, W, T, Rm, a, b, Oc, dO, wsc, tau=args.certificate_tau)
         torch.cuda.synchronize()
         c_ms = (time.perf_counter() - c0) * 1e3
         certificate = {"T": T, "R_max": Rm, "eta": [float(f"{x:.4e}") for x in eta],
                        "tau": args.certificate_tau,
-                       "selected_R": eoba.select_tail_depth(eta, args.certificate_tau),
+                       "selected_R": r_sel,
                        "ms": round(c_ms, 3), "timing": "host clock, one call (R_max + 1 backward passes)"}
         del Oc, wsc
 
@@ -452,6 +511,32 @@ def main():
         contraction = {"block": blk, "blocks": int(kappa.numel()), "delta_max": round(float(delta.max()), 4),
                        "kappa_max": round(float(kappa.max()), 4), "kappa_mean": round(float(kappa.mean()), 4),
                        "ms": round(cev[0].elapsed_time(cev[1]), 4)}
+
+    # The same inputs with the R = 4 tail (the comparison run of the
+    # long-context workload): step time, throughput and the whole path's
+    # MFMA/exp fraction counted per half-step.
+    r4 = None
+    if args.r4_steps > 0 and R != 4:
+        p4 = workloads.make(5, R=4)
+        ms4 = time_workload(eoba, torch, p4, args.r4_steps, 2, dev, tensors=(Q, K, V, dO))
+        _, _, _, f4, x4 = work_counts(prob.B, prob.H, prob.L, prob.d, W, T, 4)
+        t4 = ms4 * 1e-3
+        r4 = {"R": 4, "ms_per_step": round(ms4, 4), "tokens_per_s": round(prob.real_tokens() / t4, 1),
+              "flops": f4, "exps": x4, "frac": round(max(f4 / PEAK_MFMA[prob.dtype], x4 / PEAK_EXP) / t4, 4),
+              "steps": args.r4_steps}
+        del p4
+
+    # Step times of the other workloads (latency-bound at these sizes; the
+    # dustbin one takes per-step launches with its own kernel between them).
+    others = {}
+    if not args.no_other_configs:
+        for key, cfg, dtyp in (("tiny", 1, None), ("mid", 2, None), ("mid_bf16", 2, "bf16"),
+                               ("protein", 3, None), ("dustbin", 4, None)):
+            pc = workloads.make(cfg, dtype=dtyp)
+            msc = time_workload(eoba, torch, pc, 20, 3, dev)
+            others[key] = {"shape": list(pc.shape), "W": pc.W, "T": pc.T, "R": pc.R, "dtype": pc.dtype,
+                           "dustbin": pc.dustbin, "ms_per_step": round(msc, 4),
+                           "tokens_per_s": round(pc.real_tokens() / (msc * 1e-3), 1)}
 
     if args.copy_calibration:
         x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -470,25 +555,37 @@ def main():
     omega, ex_flops, ex_exps, sv_flops, sv_exps = work_counts(prob.B, prob.H, prob.L, prob.d, W, T, R)
     peak = PEAK_MFMA[prob.dtype]
     # Dominant kernel: the fused Sinkhorn step (T + R steps per forward, all in
-    # one persistent launch).  Its tightest roofline is HBM: each step streams
-    # every Q and K row.  Timed with HIP events around the step launch(es);
-    # figures are per Sinkhorn step.
+    # one persistent launch), timed with HIP events around its launch on the
+    # stream it runs on.  Its roofline counts the work per half-step: the row
+    # and the column update each take a score contraction (2 d flops) and an
+    # exp per band entry, so 4 d flops and 2 exps per entry per Sinkhorn step
+    # (this kernel evaluates each score once per step and reuses it for both
+    # updates), against the published bf16 MFMA and v_exp_f32 peaks.
     avg_step_s = (iter_ms / iter_launches) * 1e-3 if iter_launches else float("nan")
+    launch_steps = T + R
+    step_flops = omega * 4 * prob.d
+    step_exps = omega * 2
+    t_roof = max(step_flops / peak, step_exps / PEAK_EXP)
+    traffic = load_pmc()  # HBM bytes per Sinkhorn step (rocprofv3 counters), or None
+    roofline = {"bound": "mfma" if step_flops / peak >= step_exps / PEAK_EXP else "exp",
+                "achieved": round(step_flops * launch_steps / (avg_step_s * launch_steps) / 1e12, 2),
+                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(t_roof / avg_step_s, 4),
+                "traffic": None if traffic is None else round(traffic * launch_steps / 1e9, 3),
+                "traffic_unit": "GB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "kernel": "iter_kernel (fused Sinkhorn step; persistent: T + R steps per launch)",
+                "launch_us": round(avg_step_s * launch_steps * 1e6, 2), "steps_per_launch": launch_steps,
+                "avg_step_us": round(avg_step_s * 1e6, 3), "steps_timed": iter_launches,
+                "flops_per_launch": step_flops * launch_steps, "exps_per_launch": step_exps * launch_steps,
+                "exp_frac": round(step_exps / avg_step_s / PEAK_EXP, 4),
+                "executed_mfma_frac": round(omega * 2 * prob.d / avg_step_s / peak, 4)}
+    # the same kernel against its own HBM traffic model (Q and K streamed once
+    # per step, potentials and column partials): a separate figure
     esize = 2 if prob.dtype == "bf16" else 4
     SB, TL, TR = step_geometry(prob.B, prob.H, prob.L, W)
     step_bytes = step_bytes_per_launch(prob.B, prob.H, prob.L, prob.d, esize, SB, TL, TR)
-    step_flops = omega * 2 * prob.d
-    achieved = step_bytes / avg_step_s
-    traffic = load_pmc()
-    roofline = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
-                "traffic": None if traffic is None else round(traffic / 1e9, 4),
-                "kernel": "iter_kernel (fused Sinkhorn step; persistent: T + R steps per launch)",
-                "avg_step_us": round(avg_step_s * 1e6, 3), "steps_timed": iter_launches,
-                "bytes_per_step": int(step_bytes),
-                "traffic_unit": "GB per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "mfma_frac": round(step_flops / avg_step_s / peak, 4),
-                "exp_frac": round(omega / avg_step_s / PEAK_EXP, 4)}
+    design_hbm = {"bytes_per_step": int(step_bytes), "achieved": round(step_bytes / avg_step_s / 1e9, 1),
+                  "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(step_bytes / avg_step_s / PEAK_HBM, 4),
+                  "traffic_per_step": None if traffic is None else round(traffic / 1e9, 4)}
     t_s = ms_per_step * 1e-3
     path = {"executed": {"flops": ex_flops, "exps": ex_exps,
                          "frac": round(max(ex_flops / peak, ex_exps / PEAK_EXP) / t_s, 4)},
@@ -497,8 +594,7 @@ def main():
             "peak_mfma_flops": peak, "peak_exp_per_s": PEAK_EXP}
     if peaks is not None:
         pm, pe = peaks["mfma_bf16_flops"], peaks["exp_per_s"]
-        roofline["mfma_frac_measured"] = round(step_flops / avg_step_s / pm, 4)
-        roofline["exp_frac_measured"] = round(omega / avg_step_s / pe, 4)
+        roofline["frac_measured_peaks"] = round(max(step_flops / pm, step_exps / pe) / avg_step_s, 4)
         path["executed"]["frac_measured"] = round(max(ex_flops / pm, ex_exps / pe) / t_s, 4)
         path["survey_counting"]["frac_measured"] = round(max(sv_flops / pm, sv_exps / pe) / t_s, 4)
         path["measured_peaks"] = {"mfma_bf16_flops": float(f"{pm:.4g}"), "exp_per_s": float(f"{pe:.4g}"),
@@ -513,7 +609,11 @@ def main():
                       "B": prob.B, "H": prob.H, "L": prob.L, "d": prob.d, "W": W, "T": T, "R": R,
                       "inputs": "bf16", "accumulate": "fp32", "state": "fp64"},
            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "wall_s": round(wall, 3),
-           "roofline": roofline, "path_roofline": path}
+           "roofline": roofline, "design_hbm": design_hbm, "path_roofline": path}
+    if r4 is not None:
+        out["r4"] = r4
+    if others:
+        out["other_workloads"] = others
     if converged is not None:
         out["converged_base"] = converged
     if certificate is not None:

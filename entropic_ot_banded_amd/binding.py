@@ -21,6 +21,8 @@ SINKATTN_EINVAL = -1
 SINKATTN_EUNSUPPORTED = -2
 SINKATTN_EHIP = -3
 SINKATTN_EWORKSPACE = -4
+SINKATTN_ENONFINITE = -5
+SINKATTN_ESTALL = -6
 SINKATTN_F32 = 0
 SINKATTN_BF16 = 1
 
@@ -72,7 +74,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                       vp, vp, vp, vp, vp]
     lib.sinkattn_backward.restype = i32
     lib.sinkattn_tail_certificate.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, sz,
-                                              vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_double), vp]
+                                              vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_double),
+                                              ctypes.c_double, ctypes.POINTER(i32), vp]
     lib.sinkattn_tail_certificate.restype = i32
     lib.sinkattn_block_contraction.argtypes = [vp, vp, i32, shp, i32, vp, vp, vp]
     lib.sinkattn_block_contraction.restype = i32
@@ -281,11 +284,13 @@ def backward(Q, K, V, W: int, T: int, R: int, a, b, O, dO, workspace, lengths=No
 
 
 def tail_certificate(Q, K, V, W: int, T: int, R_max: int, a, b, O, dO, workspace, lengths=None,
-                     dustbin: bool = False):
+                     dustbin: bool = False, tau: float = 1e-5):
     """Stop-gradient bias certificate of a forward run with tail depth R_max.
-    Returns (dQ, dK, dV, eta): the gradients at depth R_max and
+    Returns (dQ, dK, dV, eta, R_selected): the gradients at depth R_max,
     eta[R] = ||grad_Rmax - grad_R|| / ||grad_Rmax|| over (dQ, dK) for
-    R = 0..R_max (see sinkattn_tail_certificate).  Blocks until done."""
+    R = 0..R_max, and the depth the library selects for tolerance tau (the
+    smallest R with eta[R] < tau, else R_max; see sinkattn_tail_certificate).
+    Blocks until done."""
     torch = _torch()
     _validate(Q, K, V, a, b, lengths)
     if dO.shape != Q.shape or dO.dtype != Q.dtype or not dO.is_contiguous():
@@ -294,13 +299,14 @@ def tail_certificate(Q, K, V, W: int, T: int, R_max: int, a, b, O, dO, workspace
     mk = lambda: torch.empty(Q.shape, dtype=torch.float32, device=Q.device)  # noqa: E731
     dQ, dK, dV, sQ, sK = mk(), mk(), mk(), mk(), mk()
     eta = (ctypes.c_double * (R_max + 1))()
+    sel = ctypes.c_int32(-1)
     s = shape.c()
     st = load_library().sinkattn_tail_certificate(
         _ptr(Q), _ptr(K), _ptr(V), W, T, R_max, _ptr(a), _ptr(b), ctypes.byref(s), _ptr(O), _ptr(dO),
-        _ptr(workspace), workspace.numel(), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(sQ), _ptr(sK), eta,
-        _stream(Q.device))
+        _ptr(workspace), workspace.numel(), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(sQ), _ptr(sK), eta, float(tau),
+        ctypes.byref(sel), _stream(Q.device))
     _check(st)
-    return dQ, dK, dV, [float(x) for x in eta]
+    return dQ, dK, dV, [float(x) for x in eta], sel.value
 
 
 def block_contraction(Q, K, W: int, block: int, lengths=None, dustbin: bool = False):
@@ -338,15 +344,6 @@ def measure_peaks(device=None) -> dict:
                                                    _stream(dev))
     _check(st)
     return {"mfma_bf16_flops": mfma.value, "exp_per_s": ex.value, "clock_hz": clk.value}
-
-
-def select_tail_depth(eta, tau: float) -> int:
-    """Smallest tail depth R whose certificate eta[R] is below tau (the
-    deepest, len(eta) - 1, when none is)."""
-    for R, e in enumerate(eta):
-        if e < tau:
-            return R
-    return len(eta) - 1
 
 
 def tail_stack(workspace, Q, R: int, lengths=None, dustbin=False):

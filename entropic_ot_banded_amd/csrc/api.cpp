@@ -6,7 +6,10 @@
 
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "../../include/sinkattn.h"
@@ -61,6 +64,12 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
   x.TL = (h1 + 15) / 16;
   x.TR = (15 + h2) / 16;
   x.NT = x.TL + x.TR + 1;
+  x.TLc = (h2 + 15) / 16;
+  x.TRc = (15 + h1) / 16;
+  x.NTc = x.TLc + x.TRc + 1;
+  // the band must fit the compiled tile counts (checked before the per-tile
+  // bit mask below is formed)
+  if (x.NT > kMaxTiles || x.NTc > kMaxTiles) return SINKATTN_EUNSUPPORTED;
   // round the row-sweep tile count up to a compiled instance (3, 5, 9, 17)
   {
     const int inst[4] = {3, 5, 9, kMaxTiles};
@@ -81,10 +90,6 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
     for (int t = 0; t < x.NT; ++t)
       if (t < x.tin_lo || t > x.tin_hi) x.edge_mask |= 1u << t;
   }
-  x.TLc = (h2 + 15) / 16;
-  x.TRc = (15 + h1) / 16;
-  x.NTc = x.TLc + x.TRc + 1;
-  if (x.TL + (15 + h2) / 16 + 1 > kMaxTiles || x.NTc > kMaxTiles) return SINKATTN_EUNSUPPORTED;
   // per-(b, h) slices are addressed with 32-bit byte offsets
   if ((long long)s->L * s->d * (s->dtype == SINKATTN_BF16 ? 2 : 4) >= (1ll << 31)) return SINKATTN_EUNSUPPORTED;
   x.nblk = (s->L + kBlockRows - 1) / kBlockRows;
@@ -126,6 +131,58 @@ TimingState& timing() {
 
 }  // namespace
 
+namespace {
+struct AttrKey {
+  int dev;
+  const void* kernel;
+  size_t lds;
+  int threads;
+  bool operator<(const AttrKey& o) const {
+    if (dev != o.dev) return dev < o.dev;
+    if (kernel != o.kernel) return kernel < o.kernel;
+    if (lds != o.lds) return lds < o.lds;
+    return threads < o.threads;
+  }
+};
+std::mutex g_attr_mu;
+std::map<AttrKey, size_t> g_lds_set;       // (dev, kernel) -> largest limit set
+std::map<AttrKey, long long> g_coop;       // (dev, kernel, lds, threads) -> resident groups
+}  // namespace
+
+hipError_t ensure_lds(const void* kernel, size_t lds) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  const AttrKey k{dev, kernel, 0, 0};
+  auto it = g_lds_set.find(k);
+  if (it != g_lds_set.end() && it->second >= lds) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) g_lds_set[k] = lds;
+  return e;
+}
+
+hipError_t coop_groups(const void* kernel, int threads, size_t lds, long long* groups) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  const AttrKey k{dev, kernel, lds, threads};
+  auto it = g_coop.find(k);
+  if (it != g_coop.end()) {
+    *groups = it->second;
+    return hipSuccess;
+  }
+  int coop = 0, cus = 0, per = 0;
+  e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, lds);
+  if (e != hipSuccess) return e;
+  *groups = coop ? (long long)per * cus : 0;
+  g_coop[k] = *groups;
+  return hipSuccess;
+}
+
 bool timing_enabled() { return timing().on; }
 
 void timing_mark(hipStream_t st, bool end, int launches) {
@@ -154,6 +211,25 @@ int hip_status(hipError_t e) {
   g_last_hip = e;
   return SINKATTN_EHIP;
 }
+
+// SINKATTN_DEBUG set to anything but "" or "0": the forward entry points
+// check their results (read once per process)
+bool debug_checks() {
+  static const bool on = [] {
+    const char* e = std::getenv("SINKATTN_DEBUG");
+    return e && e[0] && !(e[0] == '0' && e[1] == 0);
+  }();
+  return on;
+}
+
+// status of a forward launch, with the debug check's findings
+int forward_status(hipError_t e, int flags) {
+  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
+  if (e != hipSuccess) return hip_status(e);
+  if (flags & 2) return SINKATTN_ESTALL;
+  if (flags & 1) return SINKATTN_ENONFINITE;
+  return SINKATTN_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -169,6 +245,8 @@ const char* sinkattn_status_string(int status) {
     case SINKATTN_EUNSUPPORTED: return "unsupported configuration (outside the built kernels' envelope)";
     case SINKATTN_EHIP: return "HIP runtime or launch error";
     case SINKATTN_EWORKSPACE: return "workspace too small";
+    case SINKATTN_ENONFINITE: return "non-finite potentials on active tokens (SINKATTN_DEBUG check)";
+    case SINKATTN_ESTALL: return "a neighbour wait of the persistent step launch gave up: results invalid";
     default: return "unknown status";
   }
 }
@@ -243,9 +321,9 @@ int sinkattn_forward(const void* Q, const void* K, const void* V, int W, int T, 
   Workspace w = carve(static_cast<float*>(workspace), g, R);
   if (workspace_bytes < w.floats * sizeof(float)) return SINKATTN_EWORKSPACE;
   FwdLaunch f{Q, K, V, a, b, O, u, v, T, R};
-  hipError_t e = launch_forward(g, s->dtype, f, w, stream);
-  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return hip_status(e);
+  int flags = 0;
+  if (debug_checks()) f.debug_flags = &flags;
+  return forward_status(launch_forward(g, s->dtype, f, w, stream), flags);
 }
 
 int sinkattn_forward_converge(const void* Q, const void* K, const void* V, int W, int T_max, int R,
@@ -266,9 +344,9 @@ int sinkattn_forward_converge(const void* Q, const void* K, const void* V, int W
   f.stop.tol = tol;
   f.stop.T_used = T_used;
   f.stop.err_last = err_last;
-  hipError_t e = launch_forward(g, s->dtype, f, w, stream);
-  if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return hip_status(e);
+  int flags = 0;
+  if (debug_checks()) f.debug_flags = &flags;
+  return forward_status(launch_forward(g, s->dtype, f, w, stream), flags);
 }
 
 int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T, int R, const float* a,
@@ -295,11 +373,12 @@ int sinkattn_backward(const void* Q, const void* K, const void* V, int W, int T,
 int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W, int T, int R_max, const float* a,
                               const float* b, const sinkattn_shape* s, const float* O, const void* dO,
                               void* workspace, size_t workspace_bytes, float* dQ, float* dK, float* dV,
-                              float* dQ_scratch, float* dK_scratch, double* eta, hipStream_t stream) {
+                              float* dQ_scratch, float* dK_scratch, double* eta, double tau, int* R_selected,
+                              hipStream_t stream) {
   if (!Q || !K || !V || !a || !b || !O || !dO || !workspace || !dQ || !dK || !dV || !dQ_scratch ||
       !dK_scratch || !eta)
     return SINKATTN_EINVAL;
-  if (T < 0 || R_max < 1) return SINKATTN_EINVAL;
+  if (T < 0 || R_max < 1 || !(tau >= 0.0)) return SINKATTN_EINVAL;
   if (R_max > kMaxTailBackward || R_max > kMaxCertR) return SINKATTN_EUNSUPPORTED;
   Geom g;
   int st = make_geom(s, W, &g);
@@ -312,7 +391,18 @@ int sinkattn_tail_certificate(const void* Q, const void* K, const void* V, int W
   BwdLaunch f{Q, K, V, dO, O, a, b, dQ, dK, dV, nullptr, T, R_max};
   hipError_t e = launch_certificate(g, s->dtype, f, R_max, w, dQ_scratch, dK_scratch, eta, stream);
   if (e == hipErrorInvalidConfiguration) return SINKATTN_EUNSUPPORTED;
-  return hip_status(e);
+  if (e != hipSuccess) return hip_status(e);
+  if (R_selected) {
+    // the smallest depth whose residual is below tau; the deepest when none is
+    int sel = R_max;
+    for (int r = 0; r <= R_max; ++r)
+      if (eta[r] < tau) {
+        sel = r;
+        break;
+      }
+    *R_selected = sel;
+  }
+  return SINKATTN_OK;
 }
 
 int sinkattn_block_contraction(const void* Q, const void* K, int W, const sinkattn_shape* s, int block,

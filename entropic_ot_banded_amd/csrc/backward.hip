@@ -1199,8 +1199,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     return hipErrorInvalidConfiguration;
   hipError_t err;
 #define SET_LDS(kern, bytes)                                                                              \
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, \
-                            (int)(bytes));                                                                \
+  err = ensure_lds(reinterpret_cast<const void*>(kern), (size_t)(bytes));                                 \
   if (err != hipSuccess) return err;
   SET_LDS((bw_row_kernel<T, D, 1>), row_grad_lds);
   SET_LDS((bw_col_kernel<T, D, 1>), col_grad_lds);
@@ -1253,8 +1252,8 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   };
   if constexpr (kSweep) {
 #define SET_SW(COLV, MODEV, RMV, RXV)                                                                   \
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV, RMV, RXV>),   \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds(COLV, MODEV));   \
+  err = ensure_lds(reinterpret_cast<const void*>(bw_sweep_kernel<D, COLV, MODEV, RMV, RXV>),            \
+                   sweep_lds(COLV, MODEV));                                                             \
   if (err != hipSuccess) return err;
     SET_SW(false, 0, 2, false) SET_SW(false, 1, 2, false) SET_SW(true, 0, 2, false) SET_SW(true, 1, 2, false)
     SET_SW(true, 2, 2, false) SET_SW(false, 1, kMaxR, false) SET_SW(true, 1, kMaxR, false)

@@ -143,14 +143,12 @@ hipError_t launch_block_diameters(const Geom& g, int dtype, const void* Q, const
   const dim3 grid(nblocks, g.B * g.H);
   hipError_t err;
   if (dtype == 0) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(block_diameter_kernel<float>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    err = ensure_lds(reinterpret_cast<const void*>(block_diameter_kernel<float>), lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(block_diameter_kernel<float>, grid, dim3(256), lds, st, g, reinterpret_cast<const float*>(Q),
                        reinterpret_cast<const float*>(K), Bd, nblocks, delta, kappa);
   } else {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(block_diameter_kernel<bf16_t>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    err = ensure_lds(reinterpret_cast<const void*>(block_diameter_kernel<bf16_t>), lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(block_diameter_kernel<bf16_t>, grid, dim3(256), lds, st, g,
                        reinterpret_cast<const bf16_t*>(Q), reinterpret_cast<const bf16_t*>(K), Bd, nblocks, delta, kappa);

@@ -301,6 +301,8 @@ struct StepPlan {
   int* head;  // [BH * nseg] last step whose start-side boundary region a segment has written
   int* done;  // [BH * nseg] last step a segment has finished
   int* err;
+  int max_spins;  // bound of one neighbour wait
+  int wait_bias;  // added to every awaited count: 0, or (failure-path testing) a value no count reaches
 };
 
 __device__ __forceinline__ IterArgs step_args(const IterArgs& base, const StepPlan& q, int t) {
@@ -320,6 +322,11 @@ __device__ __forceinline__ IterArgs step_args(const IterArgs& base, const StepPl
 }
 
 constexpr int kMaxSpins = 1 << 20;  // bound of a neighbour wait (each spin sleeps ~256 cycles)
+// Failure-path testing (SINKATTN_DEBUG_STALL set): every neighbour wait is
+// made unsatisfiable and gives up after a few spins, so the launch still
+// runs to its end and the give-up is reported.
+constexpr int kStallTestSpins = 4;
+constexpr int kStallTestBias = 1 << 30;
 
 // One launch = one Sinkhorn step over every (b, h).  A workgroup sweeps a
 // segment of SB consecutive 128-row blocks of one sequence:
@@ -643,8 +650,10 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   // use_b), with a bounded spin that flags an error instead of hanging
   auto wait_for = [&](const int* cnt_a, int ia, bool use_a, int va, const int* cnt_b, int ib, bool use_b, int vb) {
     int spins = 0;
+    va += q.wait_bias;
+    vb += q.wait_bias;
     while ((use_a && ld_shared<true>(cnt_a + ia) < va) || (use_b && ld_shared<true>(cnt_b + ib) < vb)) {
-      if (++spins > kMaxSpins) {
+      if (++spins > q.max_spins) {
         st_shared<true>(q.err, 1);
         break;
       }
@@ -1821,6 +1830,19 @@ __global__ void step_wait_failed(const int* err, float* O, float* u) {
   }
 }
 
+// Debug content check (SINKATTN_DEBUG): counts the non-finite values among the
+// stopped base u^(0), v^(0) (fp64 tail slot 0) and the returned u, v on the
+// active tokens of every (b, h).
+__global__ void debug_scan(Geom g, const double* u0, const double* v0, const float* u, const float* v, int* count) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = real_len(g, bh / g.H) + (g.dustbin ? 1 : 0);
+  if (i >= n) return;
+  const size_t o = (size_t)bh * g.L + i;
+  const bool bad = !isfinite(u0[o]) || !isfinite(v0[o]) || !isfinite(u[o]) || !isfinite(v[o]);
+  if (bad) atomicAdd(count, 1);
+}
+
 // ---------------------------------------------------------------------------
 // Host launcher for the whole forward pass.
 // ---------------------------------------------------------------------------
@@ -1855,12 +1877,11 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
     ik = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles, false>);
     ikp = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles, true>);
   }
-  err = hipFuncSetAttribute(ik, hipFuncAttributeMaxDynamicSharedMemorySize, (int)iter_lds);
+  err = ensure_lds(ik, iter_lds);
   if (err != hipSuccess) return err;
-  err = hipFuncSetAttribute(ikp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)iter_lds);
+  err = ensure_lds(ikp, iter_lds);
   if (err != hipSuccess) return err;
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(output_kernel<T, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+  err = ensure_lds(reinterpret_cast<const void*>(output_kernel<T, D>), out_lds);
   if (err != hipSuccess) return err;
 
   if (g.dustbin) {
@@ -1959,14 +1980,11 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   bool persistent = false;
   if (N >= 2 && !g.dustbin && !stop_early && g.SB * kBlockRows >= 16 * (g.TL + g.TR) &&
       !std::getenv("SINKATTN_STEP_LAUNCHES")) {
-    int dev = 0, coop = 0, cus = 0, per = 0;
-    err = hipGetDevice(&dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, ikp, 512, iter_lds);
+    long long resident = 0;
+    err = coop_groups(ikp, 512, iter_lds, &resident);
     if (err != hipSuccess) return err;
-    if (coop && (long long)per * cus >= iter_grid) {
-      const int nprog = 2 * nbh * g.nseg + 1;
+    if (resident >= iter_grid) {
+      const int nprog = 2 * nbh * g.nseg + 2;  // counters, the error flag, the debug count
       hipLaunchKernelGGL(fill_int, dim3((nprog + 255) / 256), dim3(256), 0, st, w.prog, nprog, 0);
       IterArgs a{};
       a.Q = f.Q;
@@ -1976,8 +1994,10 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       a.sdr = w.sdr;
       a.sdc = w.sdc;
       a.padded_grid = iter_grid;
+      const bool stall_test = std::getenv("SINKATTN_DEBUG_STALL") != nullptr;
       StepPlan q{w.part, w.vbuf, w.ubuf, w.tail_u, w.tail_v, part_slot, BHL, f.T, 1, N, w.prog,
-                 w.prog + nbh * g.nseg, w.prog + 2 * nbh * g.nseg};
+                 w.prog + nbh * g.nseg, w.prog + 2 * nbh * g.nseg,
+                 stall_test ? kStallTestSpins : kMaxSpins, stall_test ? kStallTestBias : 0};
       Geom gg = g;
       void* args[] = {&gg, &a, &q};
       if (timing_enabled()) timing_mark(st, false);
@@ -2040,8 +2060,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   if constexpr (sizeof(T) == 2 && D >= 64) {
     const int NP = (g.NT + kWaves) / 2;
     const size_t sweep_lds = (size_t)8 * 32 * D * 2 + (size_t)2 * NP * 16 * 4 + 64;  // 4 pair buffers of K and V
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(output_sweep_kernel<D>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds);
+    err = ensure_lds(reinterpret_cast<const void*>(output_sweep_kernel<D>), sweep_lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((output_sweep_kernel<D>), dim3(grid), dim3(512), sweep_lds, st, g, o);
   } else {
@@ -2052,6 +2071,24 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   if (g.dustbin) {
     hipLaunchKernelGGL(dustbin_output<T>, dim3(nbh), dim3(128), 0, st, g, reinterpret_cast<const T*>(f.V),
                        w.tail_v + (size_t)f.R * BHL, o.dstate, w.sdr, f.O, f.u, f.v);
+  }
+  if (f.debug_flags) {
+    // debug check: wait for the stream, then report a wait that gave up
+    // (bit 1) and non-finite potentials (bit 0)
+    int* cnt = w.prog + 2 * nbh * g.nseg;  // [error flag, non-finite count]
+    if (!persistent) {
+      hipLaunchKernelGGL(fill_int, dim3(1), dim3(64), 0, st, cnt, 2, 0);
+    } else {
+      hipLaunchKernelGGL(fill_int, dim3(1), dim3(64), 0, st, cnt + 1, 1, 0);
+    }
+    hipLaunchKernelGGL(debug_scan, dim3((g.L + 255) / 256, nbh), dim3(256), 0, st, g, w.tail_u, w.tail_v, f.u, f.v,
+                       cnt + 1);
+    int hv[2] = {0, 0};
+    err = hipGetLastError();
+    if (err == hipSuccess) err = hipMemcpyAsync(hv, cnt, sizeof(hv), hipMemcpyDeviceToHost, st);
+    if (err == hipSuccess) err = hipStreamSynchronize(st);
+    if (err != hipSuccess) return err;
+    *f.debug_flags = (hv[0] ? 2 : 0) | (hv[1] ? 1 : 0);
   }
   return hipGetLastError();
 }

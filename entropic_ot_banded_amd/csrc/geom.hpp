@@ -63,7 +63,8 @@ struct Workspace {
   float* bw;       // backward vectors [(3R + 8) * BHL]
   double* err;     // [BH] base convergence check (row-marginal L1 error)
   double* red;     // [kRedParts][2] + [kMaxCertR + 1][4] norm reductions of the tail certificate
-  int* prog;       // [2 * BH * nseg + 1] persistent step kernel: per-segment head and done steps, then an error flag
+  int* prog;       // [2 * BH * nseg + 2] persistent step kernel: per-segment head and done steps, then an
+                   // error flag (a neighbour wait gave up) and the debug check's non-finite count
   size_t floats;
 };
 
@@ -91,10 +92,20 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.bw = take((size_t)(3 * R + 8) * BHL);
   w.err = take_d(BH);
   w.red = take_d(2 * kRedParts + 4 * (kMaxCertR + 1));
-  w.prog = reinterpret_cast<int*>(take(2 * BH * (size_t)g.nseg + 1));
+  w.prog = reinterpret_cast<int*>(take(2 * BH * (size_t)g.nseg + 2));
   w.floats = off;
   return w;
 }
+
+// Launch attributes, cached per (device, kernel) on the host so that a call
+// pays no attribute or occupancy query after the first one.
+// ensure_lds: raise the kernel's dynamic LDS limit to at least `lds` bytes
+// (hipFuncSetAttribute, once per kernel, device and larger size).
+// coop_groups: how many workgroups of `threads` threads and `lds` bytes can be
+// resident at once on the current device (occupancy x CUs), 0 when it
+// cannot launch cooperatively.
+hipError_t ensure_lds(const void* kernel, size_t lds);
+hipError_t coop_groups(const void* kernel, int threads, size_t lds, long long* groups);
 
 // Launch timing of the fused step kernel (diagnostic; see
 // sinkattn_timing_enable).  timing_mark records the start (end = false) or
@@ -124,6 +135,9 @@ struct FwdLaunch {
   float* v;
   int T, R;      // T: base steps (the maximum when stop.every > 0)
   BaseStop stop; // zero-initialised: fixed T
+  int* debug_flags;  // host int, or nullptr: when set, the launcher waits for the
+                     // stream and reports bit 0 (non-finite u^(0), v^(0), u or v on
+                     // an active token) and bit 1 (a neighbour wait gave up)
 };
 
 struct BwdLaunch {

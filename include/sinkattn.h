@@ -57,8 +57,21 @@ typedef enum {
   SINKATTN_EINVAL = -1,        /* a bad argument (NULL pointer, size, W<1, ...) */
   SINKATTN_EUNSUPPORTED = -2,  /* valid but outside the built kernels' envelope */
   SINKATTN_EHIP = -3,          /* a HIP launch or runtime call failed */
-  SINKATTN_EWORKSPACE = -4     /* workspace smaller than sinkattn_workspace_bytes */
+  SINKATTN_EWORKSPACE = -4,    /* workspace smaller than sinkattn_workspace_bytes */
+  SINKATTN_ENONFINITE = -5,    /* debug check: a non-finite potential on an active token */
+  SINKATTN_ESTALL = -6         /* a neighbour wait of the persistent step launch gave up */
 } sinkattn_status;
+
+/* Debug checks.  With the environment variable SINKATTN_DEBUG set (to
+ * anything but "" or "0"; read once per process), sinkattn_forward and
+ * sinkattn_forward_converge wait for their stream after enqueueing and check
+ * the results: SINKATTN_ESTALL when a neighbour wait of the persistent step
+ * launch gave up (the bounded spin of one workgroup waiting for another ran
+ * out: not expected, since the launch is cooperative; the outputs are then
+ * invalid), else SINKATTN_ENONFINITE when the stopped base u^(0), v^(0) or the
+ * returned u, v hold a non-finite value on an active token.  The outputs are
+ * written either way.  Without the debug checks a wait that gave up is
+ * visible only in the outputs: O[0] and u[0] are set to NaN. */
 
 /* Element type of Q, K, V and dO.  All outputs and potentials are fp32. */
 typedef enum { SINKATTN_F32 = 0, SINKATTN_BF16 = 1 } sinkattn_dtype;
@@ -185,6 +198,9 @@ int sinkattn_backward(const void *Q, const void *K, const void *V, int W, int T,
  *   dQ, dK, dV  : out, fp32 [B, H, L, d]: grad_Rmax (as sinkattn_backward).
  *   dQ_scratch, dK_scratch : device fp32 [B, H, L, d] scratch.
  *   eta         : out, host double[R_max + 1].
+ *   tau         : tolerance (>= 0) of the depth selection.
+ *   R_selected  : optional out (host int, may be NULL): the selected depth,
+ *                 the smallest R with eta[R] < tau, or R_max when none is.
  *   R_max       : 1 .. 8.
  * Runs R_max + 1 backward passes and blocks the calling thread until the
  * stream has finished them.  Argument errors return before anything is
@@ -194,7 +210,7 @@ int sinkattn_tail_certificate(const void *Q, const void *K, const void *V, int W
                               const sinkattn_shape *s, const float *O, const void *dO,
                               void *workspace, size_t workspace_bytes, float *dQ, float *dK,
                               float *dV, float *dQ_scratch, float *dK_scratch, double *eta,
-                              hipStream_t stream);
+                              double tau, int *R_selected, hipStream_t stream);
 
 /* Projective contraction diagnostic (section 2.4, second certificate): the
  * Hilbert projective diameter of every diagonal band block.  Blocks are

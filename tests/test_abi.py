@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     assert eoba.status_string(0) == "ok"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5, -6):
         assert eoba.status_string(code) not in ("ok", "unknown status")
     assert eoba.status_string(12345) == "unknown status"
     assert lib.sinkattn_version() >= 10000
@@ -180,3 +180,24 @@ def test_timing_collect_without_launches(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(FileNotFoundError):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_certificate_validation_before_launch(lib):
+    sh = _shape()
+    s = sh.c()
+    fake = ctypes.c_void_p(0x10000)
+    nb = eoba.workspace_bytes(sh, 64, 2)
+    eta = (ctypes.c_double * 9)()
+    sel = ctypes.c_int32(-3)
+
+    def call(R_max=2, tau=1e-5, e=eta):
+        return lib.sinkattn_tail_certificate(fake, fake, fake, 64, 3, R_max, fake, fake, ctypes.byref(s), fake, fake,
+                                             fake, nb, fake, fake, fake, fake, fake, e, tau, ctypes.byref(sel),
+                                             ctypes.c_void_p(None))
+
+    assert call(R_max=0) == binding.SINKATTN_EINVAL
+    assert call(R_max=9) == binding.SINKATTN_EUNSUPPORTED
+    assert call(tau=-1.0) == binding.SINKATTN_EINVAL
+    assert call(tau=float("nan")) == binding.SINKATTN_EINVAL
+    assert call(e=None) == binding.SINKATTN_EINVAL
+    assert sel.value == -3  # nothing written on a rejected call

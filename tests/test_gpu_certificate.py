@@ -56,8 +56,8 @@ def test_certificate_matches_oracle(name, mk, R_max, eta_abs, grad_tol):
     t = to_device(prob)
     O, u, v, ws = eoba.forward(t["Q"], t["K"], t["V"], prob.W, T, R_max, t["a"], t["b"], t["lengths"],
                                prob.dustbin)
-    dQ, dK, dV, eta = eoba.tail_certificate(t["Q"], t["K"], t["V"], prob.W, T, R_max, t["a"], t["b"], O,
-                                            t["dO"], ws, t["lengths"], prob.dustbin)
+    dQ, dK, dV, eta, _ = eoba.tail_certificate(t["Q"], t["K"], t["V"], prob.W, T, R_max, t["a"], t["b"], O,
+                                               t["dO"], ws, t["lengths"], prob.dustbin)
     torch.cuda.synchronize()
     eta_ref, gref = oracle.certificate_batch(prob.Q, prob.K, prob.V, prob.a, prob.b, prob.W, T, R_max,
                                              prob.dO, prob.lengths, prob.dustbin, processes=8)
@@ -75,7 +75,12 @@ def test_certificate_matches_oracle(name, mk, R_max, eta_abs, grad_tol):
         hi, lo = eta_ref[R - 1], eta_ref[R]
         if hi / lo > 1.69 and lo > 20 * eta_abs:
             tau = math.sqrt(hi * lo)
-            assert eoba.select_tail_depth(eta, tau) == oracle.select_tail_depth(eta_ref, tau) == R
+            *_, r_sel = eoba.tail_certificate(t["Q"], t["K"], t["V"], prob.W, T, R_max, t["a"], t["b"], O,
+                                              t["dO"], ws, t["lengths"], prob.dustbin, tau=tau)
+            assert r_sel == oracle.select_tail_depth(eta_ref, tau) == R
+            *_, r_none = eoba.tail_certificate(t["Q"], t["K"], t["V"], prob.W, T, R_max, t["a"], t["b"], O,
+                                               t["dO"], ws, t["lengths"], prob.dustbin, tau=0.0)
+            assert r_none == R_max  # no depth meets tau = 0
             break
     else:
         pytest.fail(f"no well-separated pair of eta values: {eta_ref}")
@@ -93,8 +98,8 @@ def test_certificate_reference_pass_equals_backward():
                                prob.dustbin)
     dQ, dK, dV, _ = eoba.backward(t["Q"], t["K"], t["V"], prob.W, prob.T, prob.R, t["a"], t["b"], O, t["dO"],
                                   ws, t["lengths"], prob.dustbin)
-    cQ, cK, cV, eta = eoba.tail_certificate(t["Q"], t["K"], t["V"], prob.W, prob.T, prob.R, t["a"], t["b"], O,
-                                            t["dO"], ws, t["lengths"], prob.dustbin)
+    cQ, cK, cV, eta, _ = eoba.tail_certificate(t["Q"], t["K"], t["V"], prob.W, prob.T, prob.R, t["a"], t["b"], O,
+                                               t["dO"], ws, t["lengths"], prob.dustbin)
     torch.cuda.synchronize()
     for a_, b_ in ((dQ, cQ), (dK, cK), (dV, cV)):
         assert torch.equal(a_, b_)
