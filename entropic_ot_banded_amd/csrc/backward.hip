@@ -705,18 +705,29 @@ __global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
     }
     return;
   }
-  // vector outputs: thread c owns column c of the head dimension
-  for (int c = tid; c < d; c += blockDim.x) {
-    float acc = 0.f;
-    for (int t = 0; t <= n; ++t) {
+  // Vector outputs over the dustbin's row (mode 3: dq_delta) or column
+  // (modes 0, 4: dv_delta, dk_delta): out[c] = sum_t w_t X_t[c].  The tokens
+  // go in chunks of 256: each thread forms the coefficient w_t of one token
+  // (the plan entry times dO (mode 0), or times the adjoint of its score),
+  // then every output column sums the chunk's weighted rows, 256 / d threads
+  // per column each taking every (256 / d)-th row; the partial sums are
+  // added in a fixed order at the end.
+  __shared__ float wch[256];
+  const int tpc = 256 / d;  // threads per output column (d divides 256)
+  const int col = tid % d, part = tid / d;
+  const T* X = mode == 0 ? dO : (mode == 3 ? K : Q);
+  float acc = 0.f;
+  for (int t0 = 0; t0 <= n; t0 += 256) {
+    const int t = t0 + tid;
+    float w = 0.f;
+    if (t <= n) {
       const size_t ot = (size_t)bh * L + t;
       if (mode == 0) {
-        acc = __builtin_fmaf(plan(t, false), Elt<T>::load(dO, ot * d + c), acc);
+        w = plan(t, false);
       } else {
         const bool row = mode == 3;
         const size_t oi = row ? od : ot, oj = row ? ot : od;
         const int bj = row ? t : n;
-        const float P = plan(t, row);
         float dP = 0.f;
         for (int cc = 0; cc < d; ++cc) dP = __builtin_fmaf(Elt<T>::load(dO, oi * d + cc), Elt<T>::load(V, oj * d + cc), dP);
         float br = dP;
@@ -727,15 +738,22 @@ __global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
           const float bm = exp2f(p.tail_v[slot(k - 1, BHL) + oj] - vR[oj]);
           br -= al * by + al * x * bm;
         }
-        const T* X = row ? K : Q;
-        acc = __builtin_fmaf(P * br, Elt<T>::load(X, ot * d + c), acc);
+        w = plan(t, row) * br;
       }
     }
-    if (mode == 0) {
-      p.out[od * d + c] = acc;
-    } else {
-      p.out[od * d + c] = acc * g.inv_sqrt_d;
-    }
+    wch[tid] = w;
+    __syncthreads();
+    const int cnt = n + 1 - t0 < 256 ? n + 1 - t0 : 256;
+    for (int k = part; k < cnt; k += tpc)
+      acc = __builtin_fmaf(wch[k], Elt<T>::load(X, ((size_t)bh * L + t0 + k) * d + col), acc);
+    __syncthreads();
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float sum = 0.f;
+    for (int k = 0; k < tpc; ++k) sum += red[col + k * d];
+    p.out[od * d + col] = mode == 0 ? sum : sum * g.inv_sqrt_d;
   }
   if (mode == 0) {
     __syncthreads();
