@@ -213,13 +213,10 @@ int hip_status(hipError_t e) {
 }
 
 // SINKATTN_DEBUG set to anything but "" or "0": the forward entry points
-// check their results (read once per process)
+// check their results (read at every call)
 bool debug_checks() {
-  static const bool on = [] {
-    const char* e = std::getenv("SINKATTN_DEBUG");
-    return e && e[0] && !(e[0] == '0' && e[1] == 0);
-  }();
-  return on;
+  const char* e = std::getenv("SINKATTN_DEBUG");
+  return e && e[0] && !(e[0] == '0' && e[1] == 0);
 }
 
 // status of a forward launch, with the debug check's findings

@@ -230,9 +230,10 @@ __device__ __forceinline__ double finish_from(const VIn& r, const DustC& dc, boo
 // takes it when the row pass's weighted column sum gamma_j leaves
 // [2^-120, 2^120]: scores spread so wide that the column's entries underflow
 // against their rows' shifts (the column-side counterpart of the row pass's
-// exact-maximum fallback).  One thread, a plain loop over the column's rows,
-// fp32 scores and an fp64 running log-sum-exp: slow, and reached only for
-// extreme inputs.
+// exact-maximum fallback).  One thread, a plain loop over the column's rows:
+// fp32 scores, an fp64 running maximum, and the sum of 2^(x_i - max) in fp32
+// (its terms are at most 1), rescaled whenever the maximum grows.  Slow, and
+// reached only for extreme inputs.
 template <typename T, bool COH>
 __device__ double exact_column_v(const Geom& g, int bh, int n, int j, const char* Qb, const char* Kb,
                                  const double* u, float bj, float sdr_j) {
@@ -242,13 +243,14 @@ __device__ double exact_column_v(const Geom& g, int bh, int n, int j, const char
   int i0 = j - g.h2, i1 = j + g.h1;
   i0 = i0 < 0 ? 0 : i0;
   i1 = i1 > n - 1 ? n - 1 : i1;
-  double m = -__builtin_inf(), s = 0.0;
+  double m = -__builtin_inf();
+  float s = 0.f;
   auto add = [&](double x) {
     if (x > m) {
-      s = s * exp2(m - x) + 1.0;
+      s = s * exp2_fast((float)(m - x)) + 1.f;
       m = x;
     } else {
-      s += exp2(x - m);
+      s += exp2_fast((float)(x - m));
     }
   };
   for (int i = i0; i <= i1; ++i) {
@@ -258,7 +260,7 @@ __device__ double exact_column_v(const Geom& g, int bh, int n, int j, const char
     add((double)(acc * g.scale2) + ld_shared<COH>(u + bh * L + i));
   }
   if (g.dustbin) add((double)sdr_j + ld_shared<COH>(u + bh * L + n));
-  return log2((double)bj) - m - log2(s);
+  return log2_split(bj) - m - log2_split(s);
 }
 
 // v^(t-1)_j from the gathered inputs, or from its exact column log-sum-exp
@@ -2023,10 +2025,20 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
       void* args[] = {&gg, &a, &q};
       if (timing_enabled()) timing_mark(st, false);
       err = hipLaunchCooperativeKernel(ikp, dim3(iter_grid), dim3(512), args, (unsigned)iter_lds, st);
-      if (err != hipSuccess) return err;
-      if (timing_enabled()) timing_mark(st, true, N);
-      persistent = true;
-      t = N + 1;
+      if (err == hipSuccess) {
+        if (timing_enabled()) timing_mark(st, true, N);
+        persistent = true;
+        t = N + 1;
+      } else if (err == hipErrorCooperativeLaunchTooLarge || err == hipErrorNotSupported) {
+        // the device refused to make every workgroup resident at once (for
+        // example while another process holds part of it): run the same
+        // steps as one launch each instead (the progress counters reset
+        // above are not used by those launches)
+        (void)hipGetLastError();
+        if (timing_enabled()) timing_mark(st, true, 0);
+      } else {
+        return err;
+      }
     }
   }
   if (persistent) {

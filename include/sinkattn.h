@@ -63,7 +63,7 @@ typedef enum {
 } sinkattn_status;
 
 /* Debug checks.  With the environment variable SINKATTN_DEBUG set (to
- * anything but "" or "0"; read once per process), sinkattn_forward and
+ * anything but "" or "0"; read at every call), sinkattn_forward and
  * sinkattn_forward_converge wait for their stream after enqueueing and check
  * the results: SINKATTN_ESTALL when a neighbour wait of the persistent step
  * launch gave up (the bounded spin of one workgroup waiting for another ran
