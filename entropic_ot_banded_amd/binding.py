@@ -23,11 +23,13 @@ SINKATTN_EHIP = -3
 SINKATTN_EWORKSPACE = -4
 SINKATTN_ENONFINITE = -5
 SINKATTN_ESTALL = -6
+SINKATTN_ESCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20  # the static device scratch of sinkattn_forward_noalloc
 SINKATTN_F32 = 0
 SINKATTN_BF16 = 1
 
 EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forward",
-            "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate",
+            "sinkattn_forward_noalloc", "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate",
             "sinkattn_block_contraction", "sinkattn_timing_enable", "sinkattn_timing_collect",
             "sinkattn_status_string", "sinkattn_last_hip_error", "sinkattn_version",
             "sinkattn_measure_peaks")
@@ -66,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sinkattn_tail_offset.restype = sz
     lib.sinkattn_forward.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, vp, sz, vp]
     lib.sinkattn_forward.restype = i32
+    lib.sinkattn_forward_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, vp, vp, vp, vp]
+    lib.sinkattn_forward_noalloc.restype = i32
     lib.sinkattn_forward_converge.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, shp, ctypes.c_double,
                                               i32, vp, vp, vp, vp, sz, ctypes.POINTER(i32),
                                               ctypes.POINTER(ctypes.c_double), vp]
@@ -228,6 +232,32 @@ def forward(Q, K, V, W: int, T: int, R: int, a, b, lengths=None, dustbin: bool =
         _ptr(v), _ptr(workspace), workspace.numel(), _stream(Q.device))
     _check(st)
     return O, u, v, workspace
+
+
+def forward_noalloc(Q, K, V, W: int, T: int, R: int, a, b, lengths=None, dustbin: bool = False, out=None):
+    """Forward pass through sinkattn_forward_noalloc: the library allocates
+    nothing (its static per-GPU scratch replaces the workspace; no tail stack
+    is returned, so there is no backward from it).  `out` = (O, u, v) lets
+    the caller supply the outputs; otherwise torch allocates them here.
+    Returns (O, u, v)."""
+    torch = _torch()
+    _validate(Q, K, V, a, b, lengths)
+    shape = _shape_of(Q, lengths, dustbin)
+    B, H, L, d = Q.shape
+    if out is None:
+        out = (torch.empty((B, H, L, d), dtype=torch.float32, device=Q.device),
+               torch.empty((B, H, L), dtype=torch.float32, device=Q.device),
+               torch.empty((B, H, L), dtype=torch.float32, device=Q.device))
+    O, u, v = out
+    if (O.shape != (B, H, L, d) or u.shape != (B, H, L) or v.shape != (B, H, L) or
+            any(t.dtype != torch.float32 or not t.is_contiguous() for t in out)):
+        raise ValueError("out must be contiguous float32 tensors [B, H, L, d], [B, H, L], [B, H, L]")
+    s = shape.c()
+    st = load_library().sinkattn_forward_noalloc(
+        _ptr(Q), _ptr(K), _ptr(V), W, T, R, _ptr(a), _ptr(b), ctypes.byref(s), _ptr(O), _ptr(u), _ptr(v),
+        _stream(Q.device))
+    _check(st)
+    return O, u, v
 
 
 def forward_converge(Q, K, V, W: int, T_max: int, R: int, a, b, tol: float, check_every: int = 1,

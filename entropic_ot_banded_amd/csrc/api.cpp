@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "../../include/sinkattn.h"
+#include "abi_internal.hpp"
 #include "geom.hpp"
 
 namespace sinkattn {
@@ -34,6 +35,8 @@ bool dtype_d_supported(int dtype, int d) {
   if (dtype == SINKATTN_BF16) return d == 32 || d == 64 || d == 128;
   return false;
 }
+
+}  // namespace
 
 // Validate the shape descriptor; fill the band geometry for band width W.
 int make_geom(const sinkattn_shape* s, int W, Geom* g) {
@@ -116,6 +119,7 @@ int make_geom(const sinkattn_shape* s, int W, Geom* g) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+namespace {
 // Diagnostic launch timing: a reusable pool of events, used in pairs.
 struct TimingState {
   bool on = false;
@@ -206,6 +210,9 @@ using namespace sinkattn;
 namespace {
 // the HIP error behind the calling thread's last SINKATTN_EHIP status
 thread_local hipError_t g_last_hip = hipSuccess;
+}  // namespace
+
+namespace sinkattn {
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return SINKATTN_OK;
   g_last_hip = e;
@@ -227,7 +234,7 @@ int forward_status(hipError_t e, int flags) {
   if (flags & 1) return SINKATTN_ENONFINITE;
   return SINKATTN_OK;
 }
-}  // namespace
+}  // namespace sinkattn
 
 extern "C" {
 
@@ -244,6 +251,7 @@ const char* sinkattn_status_string(int status) {
     case SINKATTN_EWORKSPACE: return "workspace too small";
     case SINKATTN_ENONFINITE: return "non-finite potentials on active tokens (SINKATTN_DEBUG check)";
     case SINKATTN_ESTALL: return "a neighbour wait of the persistent step launch gave up: results invalid";
+    case SINKATTN_ESCRATCH: return "the call needs more device memory than the static scratch of sinkattn_forward_noalloc";
     default: return "unknown status";
   }
 }

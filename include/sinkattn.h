@@ -59,7 +59,8 @@ typedef enum {
   SINKATTN_EHIP = -3,          /* a HIP launch or runtime call failed */
   SINKATTN_EWORKSPACE = -4,    /* workspace smaller than sinkattn_workspace_bytes */
   SINKATTN_ENONFINITE = -5,    /* debug check: a non-finite potential on an active token */
-  SINKATTN_ESTALL = -6         /* a neighbour wait of the persistent step launch gave up */
+  SINKATTN_ESTALL = -6,        /* a neighbour wait of the persistent step launch gave up */
+  SINKATTN_ESCRATCH = -7       /* sinkattn_forward_noalloc: the call needs more than its static scratch */
 } sinkattn_status;
 
 /* Debug checks.  With the environment variable SINKATTN_DEBUG set (to
@@ -134,6 +135,26 @@ int sinkattn_forward(const void *Q, const void *K, const void *V, int W, int T, 
                      const float *a, const float *b, const sinkattn_shape *s,
                      float *O, float *u, float *v, void *workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/* Forward pass that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments and outputs as sinkattn_forward, minus
+ * the workspace: the library's own static device scratch of
+ * SINKATTN_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU serves instead, so the
+ * tail stack is not handed back (this is an inference entry point: pair
+ * sinkattn_forward with sinkattn_backward for training).  The scratch is
+ * resolved once per device with hipGetSymbolAddress and kept until the
+ * process ends; every call on one GPU shares it, so calls that overlap in
+ * time on the same GPU race (serialise them, e.g. on one stream).  Every
+ * buffer the kernels rely on is cleared by the kernels themselves.
+ * Returns SINKATTN_ESCRATCH (before enqueueing anything) when the shape, W
+ * and R need more than the scratch, i.e. sinkattn_workspace_bytes(s, W, R) >
+ * SINKATTN_NOALLOC_SCRATCH_BYTES (the long-context shape B=1, H=8, L=32768,
+ * d=128, W=256 fits at R <= 4); otherwise as sinkattn_forward. */
+#define SINKATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sinkattn_forward_noalloc(const void *Q, const void *K, const void *V, int W, int T, int R,
+                             const float *a, const float *b, const sinkattn_shape *s,
+                             float *O, float *u, float *v, hipStream_t stream);
 
 /* Forward pass whose stopped base ends early once converged (section 2.1:
  * the base runs until convergence or for a fixed number of steps).

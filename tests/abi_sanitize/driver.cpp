@@ -138,7 +138,7 @@ int main() {
   long long steps = -1;
   EXPECT(sinkattn_timing_collect(&ms, &steps) == SINKATTN_OK && ms == 0.0 && steps == 0);
   EXPECT(sinkattn_timing_enable(0) == SINKATTN_OK);
-  for (int code = -6; code <= 0; ++code) EXPECT(std::strcmp(sinkattn_status_string(code), "unknown status") != 0);
+  for (int code = -7; code <= 0; ++code) EXPECT(std::strcmp(sinkattn_status_string(code), "unknown status") != 0);
   EXPECT(std::strcmp(sinkattn_status_string(99), "unknown status") == 0);
   EXPECT(sinkattn_measure_peaks(nullptr, nullptr, nullptr, nullptr) == SINKATTN_EINVAL);
   EXPECT(sinkattn_version() >= 10000);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     assert eoba.status_string(0) == "ok"
-    for code in (-1, -2, -3, -4, -5, -6):
+    for code in (-1, -2, -3, -4, -5, -6, -7):
         assert eoba.status_string(code) not in ("ok", "unknown status")
     assert eoba.status_string(12345) == "unknown status"
     assert lib.sinkattn_version() >= 10000
@@ -201,3 +201,24 @@ def test_certificate_validation_before_launch(lib):
     assert call(tau=float("nan")) == binding.SINKATTN_EINVAL
     assert call(e=None) == binding.SINKATTN_EINVAL
     assert sel.value == -3  # nothing written on a rejected call
+
+
+def test_forward_noalloc_validation_before_launch(lib):
+    """The no-allocation forward rejects bad arguments and shapes whose
+    workspace exceeds its static scratch before anything is enqueued."""
+    fake = ctypes.c_void_p(0x10000)
+
+    def call(shape, W=64, T=3, R=2, Q=fake):
+        s = shape.c()
+        return lib.sinkattn_forward_noalloc(Q, fake, fake, W, T, R, fake, fake, ctypes.byref(s), fake, fake, fake,
+                                            ctypes.c_void_p(None))
+
+    assert call(_shape(), Q=ctypes.c_void_p(None)) == binding.SINKATTN_EINVAL
+    assert call(_shape(), W=0) == binding.SINKATTN_EINVAL
+    assert call(_shape(), R=-1) == binding.SINKATTN_EINVAL
+    assert call(_shape(d=40)) == binding.SINKATTN_EUNSUPPORTED
+    big = _shape(B=1, H=64, L=32768, d=128, dtype=binding.SINKATTN_BF16)
+    assert eoba.workspace_bytes(big, 256, 2) > binding.NOALLOC_SCRATCH_BYTES
+    assert call(big, W=256) == binding.SINKATTN_ESCRATCH
+    long_ctx = _shape(B=1, H=8, L=32768, d=128, dtype=binding.SINKATTN_BF16)
+    assert eoba.workspace_bytes(long_ctx, 256, 4) <= binding.NOALLOC_SCRATCH_BYTES
