@@ -882,35 +882,39 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   const double* vR = p.tail_v + slot(R, BHL) + bh * L;
   // exponent split: strip side (x_s + ref) + window side (x_w - ref)
   const double ref = COL ? uR[s0b] : vR[s0b];
+  // Every load of the set-up reads a clamped, always valid index and the
+  // result is selected afterwards, so that the loads carry no branch: they
+  // are all in flight together instead of one round trip per condition.
   for (int c = tid; c < NWC; c += kSwThreads) {
     const int k = tw0 * 16 + c;  // window index (a column j for row sweeps, a row i for column sweeps)
     const bool ok = k >= 0 && k < n;
-    wv[c] = ok ? (float)((COL ? uR[k] : vR[k]) - ref) : kNegInf;
+    const int kc = k < 0 ? 0 : (k < n ? k : n - 1);
+    const double xw = COL ? uR[kc] : vR[kc];
+    wv[c] = ok ? (float)(xw - ref) : kNegInf;
     if (MODE == 0) {
-      float z = 0.f;
-      if (ok) {
-        if (COL)  // zz_i = alpha^(r)_i x^(r)_i
-          z = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + k] - uR[k]) * p.x[slot(p.r, BHL) + bh * L + k];
-        else  // z_j = beta^(r)_j y^(r)_j
-          z = exp2f(p.tail_v[slot(p.r, BHL) + bh * L + k] - vR[k]) * p.vbar[slot(p.r, BHL) + bh * L + k] /
-              p.b[(size_t)bb * L + k];
-      }
-      vec[c] = z;
+      float z;
+      if (COL)  // zz_i = alpha^(r)_i x^(r)_i
+        z = exp2f(p.tail_u[slot(p.r, BHL) + bh * L + kc] - xw) * p.x[slot(p.r, BHL) + bh * L + kc];
+      else  // z_j = beta^(r)_j y^(r)_j
+        z = exp2f(p.tail_v[slot(p.r, BHL) + bh * L + kc] - xw) * p.vbar[slot(p.r, BHL) + bh * L + kc] /
+            p.b[(size_t)bb * L + kc];
+      vec[c] = ok ? z : 0.f;
     } else if (MODE == 1) {
-      for (int kk = 1; kk <= R; ++kk) {
-        float m0 = 0.f, m1 = 0.f;
-        if (ok) {
+#pragma unroll
+      for (int kk = 1; kk <= RM; ++kk) {
+        if (kk <= R) {
+          float m0, m1;
           if (COL) {  // row modifiers alpha^(k)_i, alpha^(k)_i x^(k)_i
-            m0 = exp2f(p.tail_u[slot(kk, BHL) + bh * L + k] - uR[k]);
-            m1 = m0 * p.x[slot(kk, BHL) + bh * L + k];
+            m0 = exp2f(p.tail_u[slot(kk, BHL) + bh * L + kc] - xw);
+            m1 = m0 * p.x[slot(kk, BHL) + bh * L + kc];
           } else {  // column modifiers beta^(k)_j y^(k)_j, beta^(k-1)_j
-            m0 = exp2f(p.tail_v[slot(kk, BHL) + bh * L + k] - vR[k]) * p.vbar[slot(kk, BHL) + bh * L + k] /
-                 p.b[(size_t)bb * L + k];
-            m1 = exp2f(p.tail_v[slot(kk - 1, BHL) + bh * L + k] - vR[k]);
+            m0 = exp2f(p.tail_v[slot(kk, BHL) + bh * L + kc] - xw) * p.vbar[slot(kk, BHL) + bh * L + kc] /
+                 p.b[(size_t)bb * L + kc];
+            m1 = exp2f(p.tail_v[slot(kk - 1, BHL) + bh * L + kc] - xw);
           }
+          vec[(size_t)(2 * (kk - 1)) * NWC + c] = ok ? m0 : 0.f;
+          vec[(size_t)(2 * (kk - 1) + 1) * NWC + c] = ok ? m1 : 0.f;
         }
-        vec[(size_t)(2 * (kk - 1)) * NWC + c] = m0;
-        vec[(size_t)(2 * (kk - 1) + 1) * NWC + c] = m1;
       }
     }
   }
@@ -977,22 +981,28 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
       sb1[c] = sok ? a1 : (u4){0u, 0u, 0u, 0u};
     }
   }
-  // strip-side exponent part and strip modifiers (MODE 1)
-  const float sbias = sok ? (float)((COL ? vR[si] : uR[si]) + ref) : 0.f;
+  // strip-side exponent part and strip modifiers (MODE 1); clamped loads
+  // (n >= 1 here: the block holds a real row)
+  const int sil = sok ? si : n - 1;
+  const double xs = COL ? vR[sil] : uR[sil];
+  const float sbias = sok ? (float)(xs + ref) : 0.f;
   float sm0[RM], sm1[RM];  // RM >= R: tail depth bound of this instance
 #pragma unroll
   for (int k = 0; k < RM; ++k) {
     sm0[k] = 0.f;
     sm1[k] = 0.f;
-    if (MODE == 1 && k < R && sok) {
+    if (MODE == 1 && k < R) {
+      float m0, m1;
       if (COL) {  // beta^(k)_j y^(k)_j, beta^(k-1)_j
-        sm0[k] = exp2f(p.tail_v[slot(k + 1, BHL) + bh * L + si] - vR[si]) * p.vbar[slot(k + 1, BHL) + bh * L + si] /
-                 p.b[(size_t)bb * L + si];
-        sm1[k] = exp2f(p.tail_v[slot(k, BHL) + bh * L + si] - vR[si]);
+        m0 = exp2f(p.tail_v[slot(k + 1, BHL) + bh * L + sil] - xs) * p.vbar[slot(k + 1, BHL) + bh * L + sil] /
+             p.b[(size_t)bb * L + sil];
+        m1 = exp2f(p.tail_v[slot(k, BHL) + bh * L + sil] - xs);
       } else {  // alpha^(k)_i, alpha^(k)_i x^(k)_i
-        sm0[k] = exp2f(p.tail_u[slot(k + 1, BHL) + bh * L + si] - uR[si]);
-        sm1[k] = sm0[k] * p.x[slot(k + 1, BHL) + bh * L + si];
+        m0 = exp2f(p.tail_u[slot(k + 1, BHL) + bh * L + sil] - xs);
+        m1 = m0 * p.x[slot(k + 1, BHL) + bh * L + sil];
       }
+      sm0[k] = sok ? m0 : 0.f;
+      sm1[k] = sok ? m1 : 0.f;
     }
   }
 
@@ -1170,7 +1180,24 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
     const float sc = MODE == 1 ? g.inv_sqrt_d : 1.f;
     const bool fuse_e = MODE == 2 && p.e_out != nullptr;
     float e4[4] = {0.f, 0.f, 0.f, 0.f};  // E partials of the lane's four columns
-    const unsigned short* Vb = reinterpret_cast<const unsigned short*>(p.V);
+    // V at the lane's dV entries, loaded before any store (the compiler
+    // cannot move a load above a store that may alias it) from clamped rows,
+    // so that all of them are in flight at once
+    constexpr int NVL = MODE == 2 ? ND * 4 : 1;
+    unsigned short vl[NVL];
+#pragma unroll
+    for (int e = 0; e < NVL; ++e) vl[e] = 0;
+    if (fuse_e) {
+      const unsigned short* Vb = reinterpret_cast<const unsigned short*>(p.V);
+#pragma unroll
+      for (int ds = 0; ds < ND; ++ds)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = sidx0 + 4 * lg + r;
+          const int sl = s < n ? s : n - 1;
+          vl[(MODE == 2 ? ds * 4 + r : 0)] = Vb[((size_t)bh * L + sl) * D + ds * 16 + lr];
+        }
+    }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
 #pragma unroll
@@ -1178,7 +1205,7 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
         const int s = sidx0 + 4 * lg + r;
         if (s < n) {
           p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = acc[ds][r] * sc;
-          if (fuse_e) e4[r] = __builtin_fmaf(bf16_to_float(Vb[((size_t)bh * L + s) * D + ds * 16 + lr]), acc[ds][r], e4[r]);
+          if (fuse_e) e4[r] = __builtin_fmaf(bf16_to_float(vl[(MODE == 2 ? ds * 4 + r : 0)]), acc[ds][r], e4[r]);
         } else if (fuse_e && s < (int)L) {
           p.out[((size_t)bh * L + s) * D + ds * 16 + lr] = 0.f;
         }

@@ -1572,7 +1572,6 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
   constexpr int kThreads = 512;
   static_assert(CPR >= 8, "the chunk swizzle needs 8 chunks per row");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ double sh_vref;
 
   const int nbh = g.B * g.H;
   const int logical = xcd_remap(blockIdx.x, p.padded_grid);
@@ -1587,23 +1586,28 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
   const double ln2 = 0.6931471805599453;
 
   // u outputs, filler rows of u, v and O for the owned range
-  for (int c = tid; c < kBlockRows; c += kThreads) {
-    const int i = r0 + c;
-    if (i >= g.L) break;
-    if (i >= n) {
-      if (!(g.dustbin && i == n)) {
-        p.u_out[bh * L + i] = kNegInf;
-        p.v_out[bh * L + i] = kNegInf;
+  auto owned_rows = [&]() {
+    for (int c = tid; c < kBlockRows; c += kThreads) {
+      const int i = r0 + c;
+      if (i >= g.L) break;
+      if (i >= n) {
+        if (!(g.dustbin && i == n)) {
+          p.u_out[bh * L + i] = kNegInf;
+          p.v_out[bh * L + i] = kNegInf;
+        }
+      } else {
+        p.u_out[bh * L + i] = p.u_in ? (float)(p.u_in[bh * L + i] * ln2) : 0.f;
       }
-    } else {
-      p.u_out[bh * L + i] = p.u_in ? (float)(p.u_in[bh * L + i] * ln2) : 0.f;
     }
+    for (int idx = tid; idx < kBlockRows * D; idx += kThreads) {
+      const int i = r0 + idx / D;
+      if (i < g.L && i >= n && !(g.dustbin && i == n)) p.O[(bh * L + i) * D + idx % D] = 0.f;
+    }
+  };
+  if (r0 >= n) {
+    owned_rows();
+    return;
   }
-  for (int idx = tid; idx < kBlockRows * D; idx += kThreads) {
-    const int i = r0 + idx / D;
-    if (i < g.L && i >= n && !(g.dustbin && i == n)) p.O[(bh * L + i) * D + idx % D] = 0.f;
-  }
-  if (r0 >= n) return;
 
   const int NT = g.NT;
   const int NW = NT + kWaves - 1;
@@ -1612,34 +1616,63 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
   const int tw0 = blk * 8 - g.TL;
   constexpr int NBUF = 4;                                          // pair buffers: three pairs in flight
   char* tbuf = smem;                                               // [NBUF][2 tensors][32 rows][RB]
-  float* wv = reinterpret_cast<float*>(smem + NBUF * 2 * TBYTES);  // [NWC] v_j - vref
+  double* vjs = reinterpret_cast<double*>(smem + NBUF * 2 * TBYTES);  // [NWC] v_j of the window columns
+  float* wv = reinterpret_cast<float*>(vjs + NWC);                 // [NWC] v_j - vref
 
-  if (tid == 0)
-    sh_vref = p.part_in ? finish_v<bf16_t>(g, bh, n, r0, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr, p.Q, p.K,
-                                           p.u_in)
-                        : 0.0;
-  __syncthreads();
-  const double vref = sh_vref;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // The set-up's loads (Q strip, u of the strip rows, the inputs of every
+  // window column's v) are issued from clamped, always valid indices with no
+  // branch before them, so they are all in flight together; results are
+  // selected afterwards.
+  const int i0 = r0 + wave * 16;
+  const int si = i0 + lr;
+  const bool sok = si < n;
+  const int sic = sok ? si : n - 1;  // n >= 1: the block holds a real row
+  const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
+  u4 qs[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u4 q = ld16(Qb + (size_t)sic * RB + c * 64 + lg * 16);
+    qs[c] = sok ? q : (u4){0u, 0u, 0u, 0u};
+  }
+  const double ui_s = p.u_in ? p.u_in[bh * L + sic] : 0.0;
+
+  // v of the window's columns: v^(N) from the last step's column partials
+  // (zero when there was no step); the block's own columns are published
+  const DustC dc = load_dust(g, bh, p.dstate);
+  const size_t slice = (size_t)bh * L * RB;
   for (int c = tid; c < NWC; c += kThreads) {
     const int j = tw0 * 16 + c;
-    float w = kNegInf;
-    if (j >= 0 && j < n) {
-      double vj = 0.0;
-      if (p.part_in)
-        vj = finish_v<bf16_t>(g, bh, n, j, p.v_prev2, p.part_in, p.b, bb, p.dstate, p.sdr, p.Q, p.K, p.u_in);
-      if (j >= r0 && j < r0 + kBlockRows) {
-        p.v_out[bh * L + j] = (float)(vj * ln2);
-        if (p.v_tail) p.v_tail[bh * L + j] = vj;
-      }
-      w = (float)(vj - vref);
+    const int jc = j < 0 ? 0 : (j < n ? j : n - 1);
+    double vj = 0.0;
+    if (p.part_in) {
+      int slo, shi;
+      window_segments(g, jc, slo, shi);
+      vj = finish_checked<bf16_t, false>(g, gather_v_clamped(g, bh, n, jc, slo, shi, p.v_prev2, p.part_in, p.b, bb,
+                                                             p.sdr),
+                                         dc, bh, n, jc, reinterpret_cast<const char*>(p.Q) + slice,
+                                         reinterpret_cast<const char*>(p.K) + slice, p.u_in);
     }
-    wv[c] = w;
+    if (j == jc && j >= r0 && j < r0 + kBlockRows) {
+      p.v_out[bh * L + j] = (float)(vj * ln2);
+      if (p.v_tail) p.v_tail[bh * L + j] = vj;
+    }
+    vjs[c] = vj;
   }
+  owned_rows();
+  __syncthreads();
+  // the exponent split's reference: v of the block's first column (inside
+  // the window, at position 16 TL)
+  const double vref = vjs[16 * g.TL];
+  for (int c = tid; c < NWC; c += kThreads) {
+    const int j = tw0 * 16 + c;
+    wv[c] = (j >= 0 && j < n) ? (float)(vjs[c] - vref) : kNegInf;
+  }
+  const float ui2 = sok ? (float)(ui_s + vref) : 0.f;
 
   const char* Kb = reinterpret_cast<const char*>(p.K) + (size_t)bh * L * RB;
   const char* Vb = reinterpret_cast<const char*>(p.V) + (size_t)bh * L * RB;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   // K and V tile pairs stream into LDS by DMA, three pairs ahead: wave w
   // fills bytes [w KB, (w + 1) KB) of each tensor's pair buffer, and the lane
   // at chunk position pc of its row loads logical chunk pc ^ f(row), leaving
@@ -1675,18 +1708,6 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  const int i0 = r0 + wave * 16;
-  const int si = i0 + lr;
-  const bool sok = si < n;
-  const int sic = si < (int)L ? si : (int)L - 1;
-  const char* Qb = reinterpret_cast<const char*>(p.Q) + (size_t)bh * L * RB;
-  u4 qs[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const u4 q = ld16(Qb + (size_t)sic * RB + c * 64 + lg * 16);
-    qs[c] = sok ? q : (u4){0u, 0u, 0u, 0u};
-  }
-  const float ui2 = sok ? (float)((p.u_in ? p.u_in[bh * L + si] : 0.0) + vref) : 0.f;
 
   int offA2[2];
 #pragma unroll
@@ -1764,27 +1785,32 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
   }
   if (!wactive) return;
   // dustbin column term for real rows: P_i,delta V_delta
+  // (loads from clamped rows, all issued before the first store of O)
   float pd[4] = {0.f, 0.f, 0.f, 0.f};
+  float vdel[ND];
+#pragma unroll
+  for (int ds = 0; ds < ND; ++ds) vdel[ds] = 0.f;
   if (g.dustbin) {
     const double vd = p.dstate ? p.dstate[4 * bh + 1] : 0.0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + 4 * lg + r;
-      if (i < n) {
-        const double ui = p.u_in ? p.u_in[bh * L + i] : 0.0;
-        pd[r] = exp2_fast((float)((double)p.sdc[bh * L + i] + ui + vd));
-      }
+      const int ic = i < n ? i : n - 1;
+      const double ui = p.u_in ? p.u_in[bh * L + ic] : 0.0;
+      const float e = exp2_fast((float)((double)p.sdc[bh * L + ic] + ui + vd));
+      pd[r] = i < n ? e : 0.f;
     }
+    const bf16_t* Vd = reinterpret_cast<const bf16_t*>(p.V) + ((size_t)bh * L + n) * D;
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) vdel[ds] = Elt<bf16_t>::load(Vd, ds * 16 + lr);
   }
-  const bf16_t* Vbase = reinterpret_cast<const bf16_t*>(p.V) + ((size_t)bh * L + (g.dustbin ? n : 0)) * D;
 #pragma unroll
   for (int ds = 0; ds < ND; ++ds) {
     const int col = ds * 16 + lr;
-    const float vdel = g.dustbin ? Elt<bf16_t>::load(Vbase, col) : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + 4 * lg + r;
-      if (i < n) p.O[((size_t)bh * L + i) * D + col] = oacc[ds][r] + pd[r] * vdel;
+      if (i < n) p.O[((size_t)bh * L + i) * D + col] = oacc[ds][r] + pd[r] * vdel[ds];
     }
   }
 }
@@ -2092,7 +2118,7 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   o.padded_grid = grid;
   if constexpr (sizeof(T) == 2 && D >= 64) {
     const int NP = (g.NT + kWaves) / 2;
-    const size_t sweep_lds = (size_t)8 * 32 * D * 2 + (size_t)2 * NP * 16 * 4 + 64;  // 4 pair buffers of K and V
+    const size_t sweep_lds = (size_t)8 * 32 * D * 2 + (size_t)2 * NP * 16 * 12 + 64;  // 4 pair buffers of K and V, vjs, wv
     err = ensure_lds(reinterpret_cast<const void*>(output_sweep_kernel<D>), sweep_lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((output_sweep_kernel<D>), dim3(grid), dim3(512), sweep_lds, st, g, o);
