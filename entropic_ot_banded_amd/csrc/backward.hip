@@ -813,8 +813,8 @@ __global__ void dustbin_scores_bw(Geom g, const T* Q, const T* K, float* sdr, fl
 //     within 16 lanes, lane 4r + q points at 4 elements of row r, and lane c
 //     receives element c of the 4 rows).
 // Stored rows swizzle their 16-byte chunks (sw_chunk) so that both the
-// 128-bit reads of 8 consecutive rows and the transposed reads of 4
-// consecutive rows are free of bank conflicts.
+// 128-bit reads of 16 consecutive rows and the transposed reads of 4
+// consecutive rows are free of bank conflicts (256-byte rows).
 // ---------------------------------------------------------------------------
 constexpr int kSwWaves = 8;
 constexpr int kSwThreads = 64 * kSwWaves;
@@ -940,7 +940,7 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
     if (dma_wave) {
       const int pos = lane * 16;
       const int r32 = wave * RPW + pos / RB;
-      const int c = sw_chunk((pos % RB) / 16, r32);
+      const int c = sw_chunk<CPR>((pos % RB) / 16, r32);
       int row = (tw0 + 2 * pp) * 16 + r32;
       row = row < 0 ? 0 : (row >= n ? n - 1 : row);
       const uint32_t dst = lds_base + (uint32_t)((pp % NBUF) * NTEN) * TBYTES + wave * 1024;
@@ -1006,22 +1006,24 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
     }
   }
 
-  // per-lane LDS offsets: A-operand chunks of row lr; transposed B reads.
-  // The swizzle only touches the low 3 bits of a chunk index, so chunks 8
-  // apart are 128 bytes apart: two (resp. four) bases cover all of them.
-  int offA2[2];
+  // per-lane LDS offsets: A-operand chunks of row lr; transposed B reads
+  // (lane 4 r + q of its 16-lane group: row 4 lg + r, 8 bytes of chunk pair ds)
+  // The swizzle is an XOR, so sw_chunk(4 c + lg, r) = 4 c ^ sw_chunk(lg, r) and
+  // sw_chunk(2 ds + e, r) = 2 ds ^ sw_chunk(e, r).  The run-time-R dQ / dK
+  // instance has no registers to spare for offset tables and forms each
+  // offset at its read.
+  constexpr bool kTab = !(MODE == 1 && !RX);
+  const int rowA = lr * RB;
+  int hA = sw_chunk<CPR>(lg, lr) * 16;
+  const int rowB = (4 * lg + (lr >> 2)) * RB + 8 * (lr & 1);
+  int hB = sw_chunk<CPR>((lr & 3) >> 1, 4 * lg + (lr >> 2)) * 16;
+  int offA[kTab ? NCH : 1], offB[kTab ? ND : 1];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) offA2[c] = lr * RB + sw_chunk(4 * c + lg, lr) * 16;
-  auto offA = [&](int c) { return offA2[c & 1] + (c >> 1) * 128; };
-  constexpr int NB = ND < 4 ? ND : 4;
-  int offB4[NB];
-  {
-    const int m = lr;  // lane within its 16-lane group; group = lg
-    const int row = 4 * lg + (m >> 2);
+  for (int c = 0; c < (kTab ? NCH : 1); ++c) offA[c] = rowA + ((64 * c) ^ hA);
 #pragma unroll
-    for (int ds = 0; ds < NB; ++ds) offB4[ds] = row * RB + sw_chunk(2 * ds + ((m & 3) >> 1), row) * 16 + 8 * (m & 1);
-  }
-  auto offB = [&](int ds) { return offB4[ds & 3] + (ds >> 2) * 128; };
+  for (int ds = 0; ds < (kTab ? ND : 1); ++ds) offB[ds] = rowB + ((32 * ds) ^ hB);
+  auto offAat = [&](int c) { return kTab ? offA[c] : rowA + ((64 * c) ^ hA); };
+  auto offBat = [&](int ds) { return kTab ? offB[ds] : rowB + ((32 * ds) ^ hB); };
 
   float vacc = 0.f;  // MODE 0
   f4 acc[ND];
@@ -1036,6 +1038,9 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
   const bool wactive = sidx0 < n;
   for (int pp = 0; pp < NP; ++pp) {
     const int buf = pp % NBUF;
+    // (no table: keep the offset parts opaque so that the compiler does not
+    // hoist every offset out of the loop into registers)
+    if constexpr (!kTab) asm volatile("" : "+v"(hA), "+v"(hB));
     // pair pp + 3 into the buffer pair pp - 1 used (every wave is past it)
     if (pp + 3 < NP) issue_pair(pp + 3);
     // tiles 2pp, 2pp + 1 of the window; strip-relative t = window tile - wave
@@ -1055,14 +1060,14 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
         f4 sacc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const u4 a = ld16(tb0 + offA(c));
+          const u4 a = ld16(tb0 + offAat(c));
           sacc = Elt<bf16_t>::mma_chunk(sacc, a, sb0[c]);
         }
         if (MODE == 1) {
           const char* tb1 = tbuf + (size_t)(buf * NTEN + 1) * TBYTES + tt * 16 * RB;
 #pragma unroll
           for (int c = 0; c < NCH; ++c) {
-            const u4 a = ld16(tb1 + offA(c));
+            const u4 a = ld16(tb1 + offAat(c));
             dacc = Elt<bf16_t>::mma_chunk(dacc, a, sb1[c]);
           }
         }
@@ -1117,8 +1122,8 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
       const char* pb = tbuf + (size_t)(buf * NTEN + PT) * TBYTES;
 #pragma unroll
       for (int ds = 0; ds < ND; ++ds) {
-        const u2 b0 = ld_tr16(pb + offB(ds));
-        const u2 b1 = ld_tr16(pb + 16 * RB + offB(ds));
+        const u2 b0 = ld_tr16(pb + offBat(ds));
+        const u2 b1 = ld_tr16(pb + 16 * RB + offBat(ds));
         const u4 bv = {b0.x, b0.y, b1.x, b1.y};
         acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], hi, bv);
         acc[ds] = Elt<bf16_t>::mma_chunk(acc[ds], lo, bv);

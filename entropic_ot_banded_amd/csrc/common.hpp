@@ -166,13 +166,20 @@ __device__ __forceinline__ void st16(void* p, u4 v) { *reinterpret_cast<u4*>(p) 
 
 // ---------------------------------------------------------------------------
 // Streamed tile pairs in LDS (bf16 rows of RB >= 128 bytes).
-// A stored row swizzles its 16-byte chunks: chunk c of row r sits at
-// position c ^ f(r & 7), f = (r & 3) << 1 | (r >> 2) & 1, so 128-bit reads of
-// 8 consecutive rows and transposed 64-bit reads of 4 consecutive rows (the
-// two access patterns of the MFMA operands below) hit distinct banks.
+// A stored row swizzles its 16-byte chunks: chunk c of row r sits at chunk
+// position c ^ f(r).  The two read patterns of the MFMA operands are 128-bit
+// reads of one chunk in each of 16 consecutive rows and transposed 64-bit
+// reads of two chunks in each of 4 consecutive rows.  Measured on gfx950 (bank
+// conflict counter, every XOR-linear f of the row's low 4 bits): with 256-byte
+// rows (16 chunks) f(r) = (r ^ 2r) & 15 leaves both patterns free of bank
+// conflicts, while the 3-bit f = (r & 3) << 1 | (r >> 2) & 1 costs 4 conflict
+// cycles per 128-bit read and 2 per transposed read.  Rows of 8 chunks keep the
+// 3-bit f (their chunk index has 3 bits).
 // ---------------------------------------------------------------------------
+template <int CPR>
 __device__ __forceinline__ int sw_chunk(int chunk, int row) {
-  return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+  if constexpr (CPR >= 16) return chunk ^ ((row ^ (row << 1)) & 15);
+  else return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
 }
 
 // LDS address (byte offset in the workgroup's LDS) of a pointer into it.

@@ -371,7 +371,11 @@ template <typename T, int D, int NT, bool PERS>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan q) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
   constexpr int NCH = RB / 64;             // 16-byte lane chunks per row
-  constexpr int RS = RB + 16;              // LDS row: K row + 16 bytes (conflict-free lane reads)
+  // LDS row: K row + 16 bytes, which spreads the operand reads of 16
+  // consecutive rows over the banks (gfx950 still counts 4 conflict cycles per
+  // 128-bit read; a conflict-free XOR layout, which needs per-chunk lane
+  // offsets, measured slower: the tile loop is bound by its VALU issue)
+  constexpr int RS = RB + 16;
   constexpr int TILEB = 16 * RS;           // bytes per ring tile
   constexpr int PER_ROW = RB / 16;         // 16-byte chunks per row
   constexpr int NEWLD = (kBlockRows * PER_ROW + 511) / 512;  // chunks per thread per block
@@ -1686,7 +1690,7 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
     if (dma_wave) {
       const int pos = lane * 16;
       const int r32 = wave * RPW + pos / RB;
-      const int c = sw_chunk((pos % RB) / 16, r32);
+      const int c = sw_chunk<CPR>((pos % RB) / 16, r32);
       int row = (tw0 + 2 * pp) * 16 + r32;
       row = row < 0 ? 0 : (row >= n ? n - 1 : row);
       const uint32_t dst = lds_base + (uint32_t)((pp % NBUF) * 2) * TBYTES + wave * 1024;
@@ -1709,15 +1713,14 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
     asm volatile("" ::: "memory");
   };
 
-  int offA2[2];
+  int offA[NCH];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) offA2[c] = lr * RB + sw_chunk(4 * c + lg, lr) * 16;
-  constexpr int NB = ND < 4 ? ND : 4;
-  int offB4[NB];
+  for (int c = 0; c < NCH; ++c) offA[c] = lr * RB + sw_chunk<CPR>(4 * c + lg, lr) * 16;
+  int offB[ND];
   {
     const int row = 4 * lg + (lr >> 2);
 #pragma unroll
-    for (int ds = 0; ds < NB; ++ds) offB4[ds] = row * RB + sw_chunk(2 * ds + ((lr & 3) >> 1), row) * 16 + 8 * (lr & 1);
+    for (int ds = 0; ds < ND; ++ds) offB[ds] = row * RB + sw_chunk<CPR>(2 * ds + ((lr & 3) >> 1), row) * 16 + 8 * (lr & 1);
   }
 
   f4 oacc[ND];
@@ -1747,7 +1750,7 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
         f4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const u4 a = ld16(tb0 + offA2[c & 1] + (c >> 1) * 128);
+          const u4 a = ld16(tb0 + offA[c]);
           sacc = Elt<bf16_t>::mma_chunk(sacc, a, qs[c]);
         }
         const int cw = wt * 16 + 4 * lg;
@@ -1772,7 +1775,7 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
       const char* pb = tbuf + (size_t)(buf * 2 + 1) * TBYTES;
 #pragma unroll
       for (int ds = 0; ds < ND; ++ds) {
-        const int ob = offB4[ds & 3] + (ds >> 2) * 128;
+        const int ob = offB[ds];
         const u2 b0 = ld_tr16(pb + ob);
         const u2 b1 = ld_tr16(pb + 16 * RB + ob);
         const u4 bv = {b0.x, b0.y, b1.x, b1.y};
