@@ -86,7 +86,7 @@ def work_counts(B, H, L, d, W, T, R):
     contractions of 2d flops per band entry; output: score + P V (4d);
     backward: dV sweep (4d), 2R-1 vector sweeps (2d each), dQ and dK sweeps
     (score, dP and the product: 6d each).  Exps: one per entry per sweep.
-    Survey counting: one score per half-step, 2(T+R) 2d + 4d forward and
+    Half-step counting: one score per half-step, 2(T+R) 2d + 4d forward and
     (4R+10) d backward; 2(T+R) + 1 + 2R + 1 exps.
     """
     omega = B * H * band_entries_fast(L, W)
@@ -147,14 +147,29 @@ def load_pmc(launch_units=None):
 PROF_ARGS = ("--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0 --no-peaks "
              "--r4-steps 0 --no-other-configs")
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d $REPO/gpurun_out/prof/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
+             "-d $OUT/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
              + PROF_ARGS)
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
                "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS GRBM_GUI_ACTIVE")
 SQ_FILE = os.path.join(ROOT, "profiles", "iter_kernel_long_context_sq.txt")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
-           "-d $REPO/gpurun_out/prof/{sub} -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 "
+           "-d $OUT/{sub} -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 "
            + PROF_ARGS + " --copy-calibration")
+
+
+HOW = "Commands ($REPO = repository root, $OUT = output directory of the profile runs):"
+SUMMARIZE_CMD = "python3 $REPO/bench.py --summarize $OUT"
+# The persistent step launch is cooperative; rocprofv3 then ends with a
+# segmentation fault in its own teardown after the program has finished and
+# its output files are written.  The profile runs accept that status only when
+# the program printed its result line.
+EXIT_NOTE = ("  (exit status 0, or 139 from the profiler's teardown after a cooperative launch "
+             "once the program has printed its result line and the CSV files are complete)")
+TCC_COUNTERS = "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum"
+TCC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + TCC_COUNTERS + " --output-format csv "
+           "-d $OUT/tcc -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 " + PROF_ARGS)
+SWEEP_FILE = os.path.join(ROOT, "profiles", "sweep_kernels_long_context.txt")
+L2_FILE = os.path.join(ROOT, "profiles", "l2_dram_long_context.txt")
 
 
 def steps_per_dispatch(name):
@@ -177,8 +192,7 @@ def summarize(d):
     stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["Kernel statistics of the long-context workload (B=1, H=8, L=32768, d=128, W=256,",
              "T=100, R=2, bf16 inputs): 5 timed + 2 warm-up forward+backward steps.",
-             "", "Command ($REPO = repository root):", "  " + TRACE_CMD,
-             "  python3 $REPO/bench.py --summarize $REPO/gpurun_out/prof", "",
+             "", HOW, "  " + TRACE_CMD, "  " + SUMMARIZE_CMD, EXIT_NOTE, "",
              f"{'calls':>6} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
     for r in stats[:24]:
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
@@ -234,6 +248,113 @@ def summarize(d):
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     summarize_sq(d)
+    summarize_sweeps(d)
+    summarize_l2(d)
+
+
+def _per_kernel(path, names):
+    """Counter sums per dispatch, averaged per kernel name, from a rocprofv3
+    counter_collection CSV."""
+    import glob
+    files = glob.glob(os.path.join(path, "*counter_collection.csv"))
+    if not files:
+        return {}
+    per = {}
+    for r in _csv_rows(files[0]):
+        if r["Counter_Name"] not in names:
+            continue
+        key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        per.setdefault(key, {})
+        per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (k, _), v in per.items():
+        acc = out.setdefault(k, {"_n": 0})
+        acc["_n"] += 1
+        for c, x in v.items():
+            acc[c] = acc.get(c, 0.0) + x
+    return {k: {c: (x / v["_n"] if c != "_n" else x) for c, x in v.items()} for k, v in out.items()}
+
+
+def sweep_bytes(name, L=32768, H=8, d=128):
+    """HBM floor of one dispatch of an output or backward kernel at the
+    long-context workload: every tensor it streams or holds read once, its
+    fp32 output written once (bf16 tensors of L d 2 bytes per head)."""
+    t16, t32 = H * L * d * 2, H * L * d * 4
+    if "output_sweep" in name:
+        return 3 * t16 + t32                      # Q, K, V in; O out
+    if "bw_rowdot" in name:
+        return t16 + t32                          # dO, O in
+    if "bw_sweep_kernel" in name:
+        mode = int(name.split(",")[2])
+        return {0: 2 * t16, 1: 4 * t16 + t32, 2: 4 * t16 + t32}[mode]
+    return None
+
+
+def summarize_sweeps(d):
+    """Output and backward kernels: time per dispatch (trace), HBM bytes
+    (FETCH_SIZE, WRITE_SIZE, copy-calibrated) and the fraction of the HBM
+    floor their time reaches."""
+    import glob
+    stats = _csv_rows(glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))[0])
+    try:
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return
+    fetch = _per_kernel(os.path.join(d, "fetch"), {"FETCH_SIZE"})
+    write = _per_kernel(os.path.join(d, "write"), {"WRITE_SIZE"})
+    lines = ["Output and backward kernels of the long-context workload (B=1, H=8, L=32768, d=128,",
+             "W=256, R=2, bf16): time per dispatch from the kernel trace, HBM bytes per dispatch",
+             "from FETCH_SIZE and WRITE_SIZE (scaled by the 256 MiB copy calibration), and the",
+             "fraction of the kernel's HBM floor (every tensor it reads once, its fp32 output",
+             "written once, at 8 TB/s) that its time reaches.", "", HOW,
+             "  " + TRACE_CMD, "  " + PMC_CMD.format(ctr="FETCH_SIZE", sub="fetch"),
+             "  " + PMC_CMD.format(ctr="WRITE_SIZE", sub="write"), "  " + SUMMARIZE_CMD, "",
+             f"{'avg_us':>8} {'fetch_MB':>9} {'write_MB':>9} {'floor_MB':>9} {'floor_us':>9} {'frac':>6}  kernel"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        fb = sweep_bytes(name)
+        if fb is None:
+            continue
+        us = float(r["AverageNs"]) / 1e3
+        fm = fetch.get(name, {}).get("FETCH_SIZE")
+        wm = write.get(name, {}).get("WRITE_SIZE")
+        fms = f"{fm * pmc['fetch_scale'] * 1024 / 1e6:9.1f}" if fm is not None else f"{'-':>9}"
+        wms = f"{wm * pmc['write_scale'] * 1024 / 1e6:9.1f}" if wm is not None else f"{'-':>9}"
+        floor_us = fb / PEAK_HBM * 1e6
+        short = name.split("(")[0].replace("void sinkattn::", "")
+        lines.append(f"{us:8.1f} {fms} {wms} {fb / 1e6:9.1f} {floor_us:9.1f} {floor_us / us:6.3f}  {short}")
+    lines += ["", f"  kernel sources hash {kernel_source_hash()}"]
+    with open(SWEEP_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_l2(d):
+    """L2 hit rate and DRAM-bound read requests per kernel (one rocprofv3
+    --pmc pass).  TCC_EA0_RDREQ_DRAM counts the L2's read requests to the
+    memory controller side; the MI355X Infinity Cache sits behind it and has no
+    counter here, so its hits cannot be split from HBM reads."""
+    per = _per_kernel(os.path.join(d, "tcc"), set(TCC_COUNTERS.split()))
+    if not per:
+        return
+    lines = ["L2 (TCC) counters per dispatch, long-context workload (B=1, H=8, L=32768, d=128, W=256,",
+             "T=100, R=2, bf16); the persistent step kernel's dispatch covers T + R = 102 steps.", "",
+             HOW, "  " + TCC_CMD, "  " + SUMMARIZE_CMD, "",
+             f"{'hit_rate':>8} {'rdreq_M':>8} {'dram_frac':>9}  kernel"]
+    for name, v in sorted(per.items(), key=lambda kv: -kv[1].get("TCC_EA0_RDREQ_sum", 0.0)):
+        if "sinkattn" not in name:
+            continue
+        h, m = v.get("TCC_HIT_sum", 0.0), v.get("TCC_MISS_sum", 0.0)
+        rq, dr = v.get("TCC_EA0_RDREQ_sum", 0.0), v.get("TCC_EA0_RDREQ_DRAM_sum", 0.0)
+        short = name.split("(")[0].replace("void sinkattn::", "")
+        lines.append(f"{h / max(h + m, 1.0):8.3f} {rq / 1e6:8.2f} {dr / max(rq, 1.0):9.3f}  {short}")
+    lines += ["", "  hit_rate = TCC_HIT / (TCC_HIT + TCC_MISS); rdreq_M = L2 read requests to the fabric",
+              "  (millions per dispatch); dram_frac = TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ.",
+              f"  kernel sources hash {kernel_source_hash()}"]
+    with open(L2_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_sq(d):
@@ -258,11 +379,10 @@ def summarize_sq(d):
     cycles = avg["GRBM_GUI_ACTIVE"] / 8  # summed over the 8 XCDs
     simds = 256 * 4
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv "
-           "-d $REPO/gpurun_out/prof/sq -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 " + PROF_ARGS)
+           "-d $OUT/sq -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 " + PROF_ARGS)
     lines = ["Issue counters of the fused step kernel (iter_kernel), long-context workload",
              "(B=1, H=8, L=32768, d=128, W=256, T=100, R=2, bf16), per Sinkhorn step, averaged over "
-             f"{len(per)} dispatches:", "", "Command ($REPO = repository root):", "  " + cmd,
-             "  python3 $REPO/bench.py --summarize $REPO/gpurun_out/prof", ""]
+             f"{len(per)} dispatches:", "", HOW, "  " + cmd, "  " + SUMMARIZE_CMD, ""]
     for c in names:
         lines.append(f"  {c:32s} {avg[c]:16.0f}")
     mfma_busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * simds) if cycles else float("nan")
@@ -388,7 +508,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each (batch, head) problem is independent, so a batch would shard across "
               "GPUs by head with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
@@ -589,14 +709,14 @@ def main():
     t_s = ms_per_step * 1e-3
     path = {"executed": {"flops": ex_flops, "exps": ex_exps,
                          "frac": round(max(ex_flops / peak, ex_exps / PEAK_EXP) / t_s, 4)},
-            "survey_counting": {"flops": sv_flops, "exps": sv_exps,
+            "half_step_counting": {"flops": sv_flops, "exps": sv_exps,
                                 "frac": round(max(sv_flops / peak, sv_exps / PEAK_EXP) / t_s, 4)},
             "peak_mfma_flops": peak, "peak_exp_per_s": PEAK_EXP}
     if peaks is not None:
         pm, pe = peaks["mfma_bf16_flops"], peaks["exp_per_s"]
         roofline["frac_measured_peaks"] = round(max(step_flops / pm, step_exps / pe) / avg_step_s, 4)
         path["executed"]["frac_measured"] = round(max(ex_flops / pm, ex_exps / pe) / t_s, 4)
-        path["survey_counting"]["frac_measured"] = round(max(sv_flops / pm, sv_exps / pe) / t_s, 4)
+        path["half_step_counting"]["frac_measured"] = round(max(sv_flops / pm, sv_exps / pe) / t_s, 4)
         path["measured_peaks"] = {"mfma_bf16_flops": float(f"{pm:.4g}"), "exp_per_s": float(f"{pe:.4g}"),
                                   "clock_ghz": round(peaks["clock_hz"] / 1e9, 3),
                                   "probe": "sinkattn_measure_peaks: v_mfma_f32_16x16x32_bf16 and v_exp_f32 "
