@@ -485,7 +485,8 @@ def main():
     ap.add_argument("--R", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA/exp peak probes")
-    ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="heads in the oracle sample (default: one per host core, at most H and 16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSV output")
