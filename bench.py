@@ -602,7 +602,8 @@ def main():
                      "timing": "host clock, median of 5 forward_converge + backward"}
 
     # Stop-gradient bias certificate: a forward keeping R_max tail steps, then
-    # eta_R for R = 0..R_max (R_max + 1 backward passes) and the selected depth.
+    # eta_R for R = 0..R_max (one backward pass of depth R_max, then the dQ/dK sweeps of
+    # every shallower depth) and the selected depth.
     certificate = None
     if args.certificate_rmax > 0:
         Rm = args.certificate_rmax
@@ -616,7 +617,7 @@ def main():
         certificate = {"T": T, "R_max": Rm, "eta": [float(f"{x:.4e}") for x in eta],
                        "tau": args.certificate_tau,
                        "selected_R": r_sel,
-                       "ms": round(c_ms, 3), "timing": "host clock, one call (R_max + 1 backward passes)"}
+                       "ms": round(c_ms, 3), "timing": "host clock, one call (a depth-R_max backward and R_max dQ/dK sweep pairs)"}
         del Oc, wsc
 
     # Projective contraction diagnostic over the diagonal band blocks.

@@ -1256,9 +1256,18 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   SET_LDS((bw_col_kernel<T, D, 2>), col_dv_lds);
 #undef SET_LDS
 
+  // Adjoint vectors: vbar^(0..R), x^(0..R) (slot r = tail step r).  A
+  // grad-only pass of depth R reads those of a full pass of depth R_vec: the
+  // vectors of the last R tail steps do not depend on where the stop-gradient
+  // sits (each comes from the later steps only, and every modifier is taken
+  // relative to the same last step), so its slots are that pass's slots
+  // R_vec - R .. R_vec.
+  const bool grad_only = f.grad_only != 0;
+  const int Rv = grad_only ? f.R_vec : R;
+  if (grad_only && (Rv < R || f.slot0 < Rv - R)) return hipErrorInvalidValue;
   float* Dv = w.bw;
-  float* vbar = Dv + align64(BHL);
-  float* xv = vbar + align64((size_t)(R + 1) * BHL);
+  float* vbar = Dv + align64(BHL) + (size_t)(Rv - R) * BHL;
+  float* xv = Dv + align64(BHL) + align64((size_t)(Rv + 1) * BHL) + (size_t)(Rv - R) * BHL;
   BwArgs p{};
   p.Q = f.Q;
   p.K = f.K;
@@ -1284,9 +1293,9 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   const T* Kt = reinterpret_cast<const T*>(f.K);
   const T* Vt = reinterpret_cast<const T*>(f.V);
   const T* dOt = reinterpret_cast<const T*>(f.dO);
-  if (g.dustbin) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
+  if (g.dustbin && !grad_only) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
   const dim3 tok((g.L + kTokPerBlock - 1) / kTokPerBlock, nbh);
-  hipLaunchKernelGGL((bw_rowdot<T, D>), tok, dim3(256), 0, st, g, dOt, f.O, Dv);
+  if (!grad_only) hipLaunchKernelGGL((bw_rowdot<T, D>), tok, dim3(256), 0, st, g, dOt, f.O, Dv);
   // bf16 with d >= 64: streamed sweeps (one workgroup per 128-index block)
   constexpr bool kSweep = sizeof(T) == 2 && D >= 64;
   const int sgrid = (nbh * ceil_div_pos(g.L, 128) + 7) & ~7;
@@ -1310,36 +1319,38 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     SET_SW(false, 1, 2, true) SET_SW(true, 1, 2, true)
 #undef SET_SW
   }
-  // dV (band) -> add dustbin row, E, vbar^(R).  The bf16 sweep computes E and
-  // zeroes filler rows itself when there is no dustbin term to add first.
-  p.out = f.dV;
-  ps.out = f.dV;
-  const bool fuse_e = kSweep && !g.dustbin;
-  ps.e_out = fuse_e ? vbar + (size_t)R * BHL : nullptr;
-  if constexpr (kSweep)
-    hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
-  else
-    hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
-  if (!fuse_e)
-    hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, tail_u, tail_v, w.sdr, R, f.dV,
-                       vbar + (size_t)R * BHL);
-  ps.e_out = nullptr;  // the later sweeps write no E
-  if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
-  // adjoint vectors through the tail
-  for (int r = R; r >= 1; --r) {
-    p.r = r;
-    ps.r = r;
+  if (!grad_only) {
+    // dV (band) -> add dustbin row, E, vbar^(R).  The bf16 sweep computes E and
+    // zeroes filler rows itself when there is no dustbin term to add first.
+    p.out = f.dV;
+    ps.out = f.dV;
+    const bool fuse_e = kSweep && !g.dustbin;
+    ps.e_out = fuse_e ? vbar + (size_t)R * BHL : nullptr;
     if constexpr (kSweep)
-      hipLaunchKernelGGL((bw_sweep_kernel<D, false, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 0), st, g, ps);
+      hipLaunchKernelGGL((bw_sweep_kernel<D, true, 2, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 2), st, g, ps);
     else
-      hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
-    if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 1);
-    if (r > 1 || f.vbar0) {
+      hipLaunchKernelGGL((bw_col_kernel<T, D, 2>), dim3(grid), dim3(256), col_dv_lds, st, g, p);
+    if (!fuse_e)
+      hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, tail_u, tail_v, w.sdr, R, f.dV,
+                         vbar + (size_t)R * BHL);
+    ps.e_out = nullptr;  // the later sweeps write no E
+    if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
+    // adjoint vectors through the tail
+    for (int r = R; r >= 1; --r) {
+      p.r = r;
+      ps.r = r;
       if constexpr (kSweep)
-        hipLaunchKernelGGL((bw_sweep_kernel<D, true, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 0), st, g, ps);
+        hipLaunchKernelGGL((bw_sweep_kernel<D, false, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 0), st, g, ps);
       else
-        hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
-      if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 2);
+        hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
+      if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 1);
+      if (r > 1 || f.vbar0) {
+        if constexpr (kSweep)
+          hipLaunchKernelGGL((bw_sweep_kernel<D, true, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 0), st, g, ps);
+        else
+          hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
+        if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 2);
+      }
     }
   }
   // dQ, dK
@@ -1375,7 +1386,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
     hipLaunchKernelGGL((bw_col_kernel<T, D, 1>), dim3(grid), dim3(256), col_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 1>), tg, dim3(256), 0, st, g, p);
   if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 4);
-  if (f.vbar0) hipLaunchKernelGGL(bw_copy_vbar0, tg, dim3(256), 0, st, g, vbar, f.vbar0);
+  if (f.vbar0 && !grad_only) hipLaunchKernelGGL(bw_copy_vbar0, tg, dim3(256), 0, st, g, vbar, f.vbar0);
   return hipGetLastError();
 }
 

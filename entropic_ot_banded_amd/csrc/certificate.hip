@@ -7,7 +7,11 @@
 // gradient of that same N-step forward with only its last R steps
 // differentiable; it is the ordinary backward pass of depth R run on the top
 // R + 1 slots of the stack (the potentials do not depend on where the
-// stop-gradient sits).  The certificate is
+// stop-gradient sits).  Its adjoint vectors are the top R of the depth-R_max
+// pass's (each is formed from the later steps only), so after one full pass
+// every shallower gradient needs only the dQ and dK sweeps over those
+// vectors, with the tail terms of the steps below the stop-gradient left out.
+// The certificate is
 //   eta_R = ||grad_Rmax - grad_R||_F / ||grad_Rmax||_F   over (dQ, dK),
 // the gradient residual left by stopping the gradient after R steps, measured
 // against the deepest tail available (dV does not depend on R).  With T = 0 the
@@ -99,7 +103,9 @@ hipError_t launch_certificate(const Geom& g, int dtype, const BwdLaunch& base, i
     fr.R = R;
     fr.slot0 = R_max - R;
     fr.dQ = dQs;
-    fr.dK = dKs;  // dV is the same at every depth: rewritten in place
+    fr.dK = dKs;  // dV is the same at every depth: not recomputed
+    fr.grad_only = 1;
+    fr.R_vec = R_max;
     err = launch_backward(g, dtype, fr, w, st);
     if (err != hipSuccess) return err;
     const float* pairs[2][2] = {{dQs, base.dQ}, {dKs, base.dK}};

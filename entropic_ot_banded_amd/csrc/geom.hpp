@@ -155,6 +155,9 @@ struct BwdLaunch {
   int T, R;
   int slot0;  // tail-stack slot of this pass's u^(0), v^(0): R_fwd - R when the
               // forward kept a deeper tail R_fwd (0 otherwise)
+  int grad_only;  // nonzero: only dQ and dK, from the adjoint vectors that a full
+                  // pass of depth R_vec (>= R, same forward) left in the workspace
+  int R_vec;
 };
 
 }  // namespace sinkattn

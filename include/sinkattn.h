@@ -223,9 +223,11 @@ int sinkattn_backward(const void *Q, const void *K, const void *V, int W, int T,
  *   R_selected  : optional out (host int, may be NULL): the selected depth,
  *                 the smallest R with eta[R] < tau, or R_max when none is.
  *   R_max       : 1 .. 8.
- * Runs R_max + 1 backward passes and blocks the calling thread until the
- * stream has finished them.  Argument errors return before anything is
- * enqueued. */
+ * Runs one backward pass of depth R_max and, for every shallower depth, the
+ * dQ and dK sweeps over that pass's adjoint vectors (the last R tail steps'
+ * vectors do not depend on where the stop-gradient sits), then blocks the
+ * calling thread until the stream has finished them.  Argument errors return
+ * before anything is enqueued. */
 int sinkattn_tail_certificate(const void *Q, const void *K, const void *V, int W, int T,
                               int R_max, const float *a, const float *b,
                               const sinkattn_shape *s, const float *O, const void *dO,
