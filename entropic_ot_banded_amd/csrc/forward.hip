@@ -631,6 +631,19 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   };
 
   const char* lane_k = kw + lr * RS + lg * 16;  // lane's operand bytes in ring row lr
+  // Additive band masks of the strip's first and last tiles (0 inside the
+  // band, -inf outside, full rows): when those are the only tiles crossing a
+  // band edge, a full strip masks them with four adds instead of the
+  // per-entry offset test.
+  float mb0[4], mb1[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int o0 = -g.TL * 16 + lr - 4 * lg - r;
+    const int o1 = (NT - 1 - g.TL) * 16 + lr - 4 * lg - r;
+    mb0[r] = (o0 >= -g.h1 && o0 <= g.h2) ? 0.f : kNegInf;
+    mb1[r] = (o1 >= -g.h1 && o1 <= g.h2) ? 0.f : kNegInf;
+  }
+  const bool ends_only = (g.edge_mask & ~(1u | (1u << (NT - 1)))) == 0u;
   const float* lane_wv = wv + lr;               // w of the lane's tile column
   int jpend = -1;                               // entering column whose v is not yet stored
   double vpend = 0.0;
@@ -797,6 +810,16 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           x[r] = ok ? x[r] : kNegInf;
         }
       };
+      // the band mask of tile t (emask bit t set)
+      const bool fast_ends = ends_only && !partial;
+      auto mask_tile = [&](int t, float (&x)[4]) {
+        if ((t == 0 || t == NT - 1) && fast_ends) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] += t == 0 ? mb0[r] : mb1[r];
+        } else {
+          masked(t, x);
+        }
+      };
       auto read_tile = [&](int t, u4 (&kb)[NCH], float& w) {
         const int sl = wrap(sw + t);
         const char* src = lane_k + sl * TILEB;
@@ -826,7 +849,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           float x[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(acc[r], g.scale2, w);
-          if ((emask >> t) & 1u) masked(t, x);
+          if ((emask >> t) & 1u) mask_tile(t, x);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             e[t][r] = exp2_fast(x[r]);
@@ -894,7 +917,7 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           const f4 acc = mma_tile(kb);
 #pragma unroll
           for (int r = 0; r < 4; ++r) e[t][r] = __builtin_fmaf(acc[r], g.scale2, w);
-          if ((emask >> t) & 1u) masked(t, e[t]);
+          if ((emask >> t) & 1u) mask_tile(t, e[t]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) m[r] = fmaxf(m[r], e[t][r]);
         }
