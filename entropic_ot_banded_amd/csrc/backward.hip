@@ -638,14 +638,22 @@ __global__ void bw_finish_grad(Geom g, BwArgs p) {
   for (int c = 0; c < d; ++c) p.out[o * d + c] = __builtin_fmaf(dS, Elt<T>::load(X, ox * d + c), p.out[o * d + c]);
 }
 
-// Dustbin row and column (full length), one workgroup per (b, h).
+// Dustbin row and column (full length).
 //   mode 0: dV_delta = sum_i P_i,delta dO_i, vbar^(R)_delta = V_delta . dV_delta
 //   mode 1: x^(r)_delta (row pass r)
 //   mode 2: vbar^(r-1)_delta (column pass r)
 //   mode 3: dQ_delta (row),  mode 4: dK_delta (column)
+// The tokens go in chunks of 256, one workgroup per (chunk, (b, h)): each
+// thread forms the coefficient w_t of one token (modes 1, 2: its term of the
+// sum; modes 0, 3, 4: the plan entry times dO (mode 0), or times the adjoint
+// of its score), and the chunk's partial sum goes to `dpart` (modes 1, 2: one
+// value; modes 0, 3, 4: out[c] = sum_t w_t X_t[c], 256 / d threads per column
+// c each taking every (256 / d)-th token).  bw_dustbin_fin then adds the
+// chunks in a fixed order and finishes the output.
 template <typename T>
-__global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(256) void bw_dustbin_part(Geom g, BwArgs p, int mode, float* dpart) {
+  const int bh = blockIdx.y;
+  const int chunk = blockIdx.x;
   const int bb = bh / g.H;
   const int n = real_len(g, bb);
   const size_t L = g.L;
@@ -653,6 +661,9 @@ __global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
   const int d = g.d;
   const int R = p.R;
   const int tid = threadIdx.x;
+  const int t0 = chunk * 256;
+  float* out = dpart + ((size_t)bh * gridDim.x + chunk) * d;
+  if (t0 > n) return;  // a chunk past the dustbin (the finish reads only the chunks up to it)
   const size_t od = (size_t)bh * L + n;
   const double* uR = p.tail_u + slot(R, BHL);
   const double* vR = p.tail_v + slot(R, BHL);
@@ -664,36 +675,90 @@ __global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
   // plan entry with the dustbin: row side (delta, t) when row = true
   auto plan = [&](int t, bool row) {
     const size_t ot = (size_t)bh * L + t;
-    const float s = row ? p.sdr[ot] : p.sdc[ot];
-    return row ? exp2f(s + uR[od] + vR[ot]) : exp2f(s + uR[ot] + vR[od]);
+    const float sc = row ? p.sdr[ot] : p.sdc[ot];
+    return row ? exp2f(sc + uR[od] + vR[ot]) : exp2f(sc + uR[ot] + vR[od]);
   };
-  auto block_sum = [&](float v) {
-    red[tid] = v;
+  const int t = t0 + tid;
+  const size_t ot = (size_t)bh * L + t;
+  float w = 0.f;
+  if (t <= n) {
+    if (mode == 1) {  // z_t = beta^(r)_t y^(r)_t over the dustbin row
+      const int r = p.r;
+      const float z = exp2f(p.tail_v[slot(r, BHL) + ot] - vR[ot]) * p.vbar[slot(r, BHL) + ot] / p.b[(size_t)bb * L + t];
+      w = plan(t, true) * z;
+    } else if (mode == 2) {  // zz_t = alpha^(r)_t x^(r)_t over the dustbin column
+      const int r = p.r;
+      const float z = exp2f(p.tail_u[slot(r, BHL) + ot] - uR[ot]) * p.x[slot(r, BHL) + ot];
+      w = plan(t, false) * z;
+    } else if (mode == 0) {
+      w = plan(t, false);
+    } else {
+      const bool row = mode == 3;
+      const size_t oi = row ? od : ot, oj = row ? ot : od;
+      const int bj = row ? t : n;
+      float dP = 0.f;
+      for (int cc = 0; cc < d; ++cc) dP = __builtin_fmaf(Elt<T>::load(dO, oi * d + cc), Elt<T>::load(V, oj * d + cc), dP);
+      float br = dP;
+      for (int k = 1; k <= R; ++k) {
+        const float al = exp2f(p.tail_u[slot(k, BHL) + oi] - uR[oi]);
+        const float x = p.x[slot(k, BHL) + oi];
+        const float by = exp2f(p.tail_v[slot(k, BHL) + oj] - vR[oj]) * p.vbar[slot(k, BHL) + oj] / p.b[(size_t)bb * L + bj];
+        const float bm = exp2f(p.tail_v[slot(k - 1, BHL) + oj] - vR[oj]);
+        br -= al * by + al * x * bm;
+      }
+      w = plan(t, row) * br;
+    }
+  }
+  if (mode == 1 || mode == 2) {
+    red[tid] = w;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if (tid < s) red[tid] += red[tid + s];
+    for (int sft = 128; sft > 0; sft >>= 1) {
+      if (tid < sft) red[tid] += red[tid + sft];
       __syncthreads();
     }
-    const float r = red[0];
-    __syncthreads();
-    return r;
-  };
+    if (tid == 0) out[0] = red[0];
+    return;
+  }
+  __shared__ float wch[256];
+  const int tpc = 256 / d;  // threads per output column (d divides 256)
+  const int col = tid % d, part = tid / d;
+  const T* X = mode == 0 ? dO : (mode == 3 ? K : Q);
+  wch[tid] = w;
+  __syncthreads();
+  const int cnt = n + 1 - t0 < 256 ? n + 1 - t0 : 256;
+  float acc = 0.f;
+  for (int k = part; k < cnt; k += tpc) acc = __builtin_fmaf(wch[k], Elt<T>::load(X, ((size_t)bh * L + t0 + k) * d + col), acc);
+  red[tid] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float sum = 0.f;
+    for (int k = 0; k < tpc; ++k) sum += red[col + k * d];
+    out[col] = sum;
+  }
+}
+
+// The chunks of bw_dustbin_part added in chunk order, and the outputs of
+// each mode.  One workgroup per (b, h).
+template <typename T>
+__global__ __launch_bounds__(256) void bw_dustbin_fin(Geom g, BwArgs p, int mode, const float* dpart, int nch) {
+  const int bh = blockIdx.x;
+  const int bb = bh / g.H;
+  const int n = real_len(g, bb);
+  const size_t L = g.L;
+  const size_t BHL = (size_t)g.B * g.H * L;
+  const int d = g.d;
+  const int R = p.R;
+  const int tid = threadIdx.x;
+  const size_t od = (size_t)bh * L + n;
+  const int used = (n + 1 + 255) / 256;  // chunks holding the dustbin's tokens 0 .. n
+  const float* in = dpart + (size_t)bh * nch * d;
   if (mode == 1 || mode == 2) {
-    const int r = p.r;
-    float acc = 0.f;
-    for (int t = tid; t <= n; t += blockDim.x) {
-      const size_t ot = (size_t)bh * L + t;
-      if (mode == 1) {
-        // z_t = beta^(r)_t y^(r)_t over the dustbin row
-        const float z = exp2f(p.tail_v[slot(r, BHL) + ot] - vR[ot]) * p.vbar[slot(r, BHL) + ot] / p.b[(size_t)bb * L + t];
-        acc += plan(t, true) * z;
-      } else {
-        const float z = exp2f(p.tail_u[slot(r, BHL) + ot] - uR[ot]) * p.x[slot(r, BHL) + ot];
-        acc += plan(t, false) * z;
-      }
-    }
-    acc = block_sum(acc);
     if (tid == 0) {
+      float acc = 0.f;
+      for (int c = 0; c < used; ++c) acc += in[(size_t)c * d];
+      const int r = p.r;
+      const double* uR = p.tail_u + slot(R, BHL);
+      const double* vR = p.tail_v + slot(R, BHL);
       if (mode == 1) {
         const float alpha = exp2f(p.tail_u[slot(r, BHL) + od] - uR[od]);
         const float ub = (r == R ? p.D[od] : 0.f) - alpha * acc;
@@ -705,62 +770,24 @@ __global__ __launch_bounds__(256) void bw_dustbin(Geom g, BwArgs p, int mode) {
     }
     return;
   }
-  // Vector outputs over the dustbin's row (mode 3: dq_delta) or column
-  // (modes 0, 4: dv_delta, dk_delta): out[c] = sum_t w_t X_t[c].  The tokens
-  // go in chunks of 256: each thread forms the coefficient w_t of one token
-  // (the plan entry times dO (mode 0), or times the adjoint of its score),
-  // then every output column sums the chunk's weighted rows, 256 / d threads
-  // per column each taking every (256 / d)-th row; the partial sums are
-  // added in a fixed order at the end.
-  __shared__ float wch[256];
-  const int tpc = 256 / d;  // threads per output column (d divides 256)
-  const int col = tid % d, part = tid / d;
-  const T* X = mode == 0 ? dO : (mode == 3 ? K : Q);
-  float acc = 0.f;
-  for (int t0 = 0; t0 <= n; t0 += 256) {
-    const int t = t0 + tid;
-    float w = 0.f;
-    if (t <= n) {
-      const size_t ot = (size_t)bh * L + t;
-      if (mode == 0) {
-        w = plan(t, false);
-      } else {
-        const bool row = mode == 3;
-        const size_t oi = row ? od : ot, oj = row ? ot : od;
-        const int bj = row ? t : n;
-        float dP = 0.f;
-        for (int cc = 0; cc < d; ++cc) dP = __builtin_fmaf(Elt<T>::load(dO, oi * d + cc), Elt<T>::load(V, oj * d + cc), dP);
-        float br = dP;
-        for (int k = 1; k <= R; ++k) {
-          const float al = exp2f(p.tail_u[slot(k, BHL) + oi] - uR[oi]);
-          const float x = p.x[slot(k, BHL) + oi];
-          const float by = exp2f(p.tail_v[slot(k, BHL) + oj] - vR[oj]) * p.vbar[slot(k, BHL) + oj] / p.b[(size_t)bb * L + bj];
-          const float bm = exp2f(p.tail_v[slot(k - 1, BHL) + oj] - vR[oj]);
-          br -= al * by + al * x * bm;
-        }
-        w = plan(t, row) * br;
-      }
-    }
-    wch[tid] = w;
-    __syncthreads();
-    const int cnt = n + 1 - t0 < 256 ? n + 1 - t0 : 256;
-    for (int k = part; k < cnt; k += tpc)
-      acc = __builtin_fmaf(wch[k], Elt<T>::load(X, ((size_t)bh * L + t0 + k) * d + col), acc);
-    __syncthreads();
-  }
-  red[tid] = acc;
-  __syncthreads();
-  if (part == 0) {
+  __shared__ float outv[256];
+  __shared__ float red[256];
+  for (int c = tid; c < d; c += 256) {
     float sum = 0.f;
-    for (int k = 0; k < tpc; ++k) sum += red[col + k * d];
-    p.out[od * d + col] = mode == 0 ? sum : sum * g.inv_sqrt_d;
+    for (int k = 0; k < used; ++k) sum += in[(size_t)k * d + c];
+    outv[c] = mode == 0 ? sum : sum * g.inv_sqrt_d;
+    p.out[od * d + c] = outv[c];
   }
-  if (mode == 0) {
+  if (mode == 0) {  // vbar^(R)_delta = E_delta = V_delta . dV_delta
     __syncthreads();
-    float e = 0.f;
-    for (int c = tid; c < d; c += blockDim.x) e = __builtin_fmaf(Elt<T>::load(V, od * d + c), p.out[od * d + c], e);
-    e = block_sum(e);
-    if (tid == 0) p.vbar[slot(R, BHL) + od] = e;
+    const T* V = reinterpret_cast<const T*>(p.V);
+    red[tid] = tid < d ? Elt<T>::load(V, od * d + tid) * outv[tid] : 0.f;
+    __syncthreads();
+    for (int sft = 128; sft > 0; sft >>= 1) {
+      if (tid < sft) red[tid] += red[tid + sft];
+      __syncthreads();
+    }
+    if (tid == 0) p.vbar[slot(R, BHL) + od] = red[0];
   }
 }
 
@@ -1294,6 +1321,13 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   const T* Vt = reinterpret_cast<const T*>(f.V);
   const T* dOt = reinterpret_cast<const T*>(f.dO);
   if (g.dustbin && !grad_only) hipLaunchKernelGGL(dustbin_scores_bw<T>, tg, dim3(256), 0, st, g, Qt, Kt, w.sdr, w.sdc);
+  // dustbin row / column sums: chunk partials, then the fixed-order finish
+  const int dch = (g.L + 255) / 256;
+  float* dpart = w.dpart;
+  auto dustbin_bw = [&](int mode) {
+    hipLaunchKernelGGL(bw_dustbin_part<T>, dim3(dch, nbh), dim3(256), 0, st, g, p, mode, dpart);
+    hipLaunchKernelGGL(bw_dustbin_fin<T>, dim3(nbh), dim3(256), 0, st, g, p, mode, static_cast<const float*>(dpart), dch);
+  };
   const dim3 tok((g.L + kTokPerBlock - 1) / kTokPerBlock, nbh);
   if (!grad_only) hipLaunchKernelGGL((bw_rowdot<T, D>), tok, dim3(256), 0, st, g, dOt, f.O, Dv);
   // bf16 with d >= 64: streamed sweeps (one workgroup per 128-index block)
@@ -1334,7 +1368,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
       hipLaunchKernelGGL(bw_finish_dv<T>, tok, dim3(256), 0, st, g, Vt, dOt, tail_u, tail_v, w.sdr, R, f.dV,
                          vbar + (size_t)R * BHL);
     ps.e_out = nullptr;  // the later sweeps write no E
-    if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 0);
+    if (g.dustbin) dustbin_bw(0);
     // adjoint vectors through the tail
     for (int r = R; r >= 1; --r) {
       p.r = r;
@@ -1343,13 +1377,13 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
         hipLaunchKernelGGL((bw_sweep_kernel<D, false, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(false, 0), st, g, ps);
       else
         hipLaunchKernelGGL((bw_row_kernel<T, D, 0>), dim3(grid), dim3(256), row_vec_lds, st, g, p);
-      if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 1);
+      if (g.dustbin) dustbin_bw(1);
       if (r > 1 || f.vbar0) {
         if constexpr (kSweep)
           hipLaunchKernelGGL((bw_sweep_kernel<D, true, 0, 2>), dim3(sgrid), dim3(kSwThreads), sweep_lds(true, 0), st, g, ps);
         else
           hipLaunchKernelGGL((bw_col_kernel<T, D, 0>), dim3(grid), dim3(256), col_vec_lds, st, g, p);
-        if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 2);
+        if (g.dustbin) dustbin_bw(2);
       }
     }
   }
@@ -1369,7 +1403,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   else
     hipLaunchKernelGGL((bw_row_kernel<T, D, 1>), dim3(grid), dim3(256), row_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 0>), tg, dim3(256), 0, st, g, p);
-  if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 3);
+  if (g.dustbin) dustbin_bw(3);
   p.out = f.dK;
   ps.out = f.dK;
   if constexpr (kSweep) {
@@ -1385,7 +1419,7 @@ static hipError_t backward_impl(const Geom& g, const BwdLaunch& f, const Workspa
   else
     hipLaunchKernelGGL((bw_col_kernel<T, D, 1>), dim3(grid), dim3(256), col_grad_lds, st, g, p);
   hipLaunchKernelGGL((bw_finish_grad<T, 1>), tg, dim3(256), 0, st, g, p);
-  if (g.dustbin) hipLaunchKernelGGL(bw_dustbin<T>, dim3(nbh), dim3(256), 0, st, g, p, 4);
+  if (g.dustbin) dustbin_bw(4);
   if (f.vbar0 && !grad_only) hipLaunchKernelGGL(bw_copy_vbar0, tg, dim3(256), 0, st, g, vbar, f.vbar0);
   return hipGetLastError();
 }

@@ -1843,49 +1843,66 @@ __global__ __launch_bounds__(512) void output_sweep_kernel(Geom g, OutArgs p) {
 
 // Dustbin row of the output: O_delta = sum_j P_delta,j V_j over active j,
 // plus u, v of the dustbin (state fp64 log2 units, outputs natural).
-// One workgroup of 256 threads per (b, h).  Columns go in chunks of 256: each
+// The columns go in chunks of 256, one workgroup per (chunk, (b, h)): each
 // thread forms the plan entry of one column, then every output element sums
 // the chunk's weighted V rows (256 / d threads per element, each taking every
-// (256 / d)-th row); the partial sums are added in a fixed order at the end.
+// (256 / d)-th row) into `dpart`; dustbin_output_fin adds the chunks in a
+// fixed order.
 template <typename T>
-__global__ __launch_bounds__(256) void dustbin_output(Geom g, const T* V, const double* v2_real,
-                                                      const double* dstate, const float* sdr,
-                                                      float* O, float* u_out, float* v_out) {
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(256) void dustbin_output_part(Geom g, const T* V, const double* v2_real,
+                                                           const double* dstate, const float* sdr, float* dpart) {
+  const int bh = blockIdx.y;
+  const int chunk = blockIdx.x;
   const int n = real_len(g, bh / g.H);
   const size_t L = g.L;
   const int d = g.d;
   const int tid = threadIdx.x;
+  const int j0 = chunk * 256;
+  if (j0 > n) return;  // past the dustbin: the finish reads only the chunks up to it
   const double ud = dstate ? dstate[4 * bh + 0] : 0.0;
   const double vd = dstate ? dstate[4 * bh + 1] : 0.0;
   __shared__ float wch[256];
   __shared__ float red[256];
   const int tpc = 256 / d;  // d divides 256
   const int col = tid % d, part = tid / d;
-  float acc = 0.f;
-  for (int j0 = 0; j0 <= n; j0 += 256) {
-    const int j = j0 + tid;
-    float w = 0.f;
-    if (j <= n) {
-      const double vj = (j == n) ? vd : v2_real[bh * L + j];
-      w = exp2_fast((float)((double)sdr[bh * L + j] + ud + vj));
-    }
-    wch[tid] = w;
-    __syncthreads();
-    const int cnt = n + 1 - j0 < 256 ? n + 1 - j0 : 256;
-    for (int k = part; k < cnt; k += tpc)
-      acc = __builtin_fmaf(wch[k], Elt<T>::load(V, ((size_t)bh * L + j0 + k) * d + col), acc);
-    __syncthreads();
+  const int j = j0 + tid;
+  float w = 0.f;
+  if (j <= n) {
+    const double vj = (j == n) ? vd : v2_real[bh * L + j];
+    w = exp2_fast((float)((double)sdr[bh * L + j] + ud + vj));
   }
+  wch[tid] = w;
+  __syncthreads();
+  const int cnt = n + 1 - j0 < 256 ? n + 1 - j0 : 256;
+  float acc = 0.f;
+  for (int k = part; k < cnt; k += tpc) acc = __builtin_fmaf(wch[k], Elt<T>::load(V, ((size_t)bh * L + j0 + k) * d + col), acc);
   red[tid] = acc;
   __syncthreads();
   if (part == 0) {
     float sum = 0.f;
     for (int k = 0; k < tpc; ++k) sum += red[col + k * d];
-    O[((size_t)bh * L + n) * d + col] = sum;
+    dpart[((size_t)bh * gridDim.x + chunk) * d + col] = sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void dustbin_output_fin(Geom g, const double* dstate, const float* dpart, int nch,
+                                                          float* O, float* u_out, float* v_out) {
+  const int bh = blockIdx.x;
+  const int n = real_len(g, bh / g.H);
+  const size_t L = g.L;
+  const int d = g.d;
+  const int tid = threadIdx.x;
+  const int used = (n + 1 + 255) / 256;
+  const float* in = dpart + (size_t)bh * nch * d;
+  for (int c = tid; c < d; c += 256) {
+    float sum = 0.f;
+    for (int k = 0; k < used; ++k) sum += in[(size_t)k * d + c];
+    O[((size_t)bh * L + n) * d + c] = sum;
   }
   if (tid == 0) {
     const double ln2 = 0.6931471805599453;
+    const double ud = dstate ? dstate[4 * bh + 0] : 0.0;
+    const double vd = dstate ? dstate[4 * bh + 1] : 0.0;
     u_out[bh * L + n] = (float)(ud * ln2);
     v_out[bh * L + n] = (float)(vd * ln2);
   }
@@ -2154,8 +2171,11 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   if (persistent)
     hipLaunchKernelGGL(step_wait_failed, dim3(1), dim3(1), 0, st, w.prog + 2 * nbh * g.nseg, f.O, f.u);
   if (g.dustbin) {
-    hipLaunchKernelGGL(dustbin_output<T>, dim3(nbh), dim3(256), 0, st, g, reinterpret_cast<const T*>(f.V),
-                       w.tail_v + (size_t)f.R * BHL, o.dstate, w.sdr, f.O, f.u, f.v);
+    const int dch = (g.L + 255) / 256;
+    hipLaunchKernelGGL(dustbin_output_part<T>, dim3(dch, nbh), dim3(256), 0, st, g, reinterpret_cast<const T*>(f.V),
+                       w.tail_v + (size_t)f.R * BHL, o.dstate, w.sdr, w.dpart);
+    hipLaunchKernelGGL(dustbin_output_fin, dim3(nbh), dim3(256), 0, st, g, o.dstate,
+                       static_cast<const float*>(w.dpart), dch, f.O, f.u, f.v);
   }
   if (f.debug_flags) {
     // debug check: wait for the stream, then report a wait that gave up

@@ -65,6 +65,7 @@ struct Workspace {
   double* red;     // [kRedParts][2] + [kMaxCertR + 1][4] norm reductions of the tail certificate
   int* prog;       // [2 * BH * nseg + 2] persistent step kernel: per-segment head and done steps, then an
                    // error flag (a neighbour wait gave up) and the debug check's non-finite count
+  float* dpart;    // [BH][ceil(L / 256)][d] dustbin row / column sums per chunk of 256 tokens (dustbin only)
   size_t floats;
 };
 
@@ -93,6 +94,7 @@ inline Workspace carve(float* base, const Geom& g, int R) {
   w.err = take_d(BH);
   w.red = take_d(2 * kRedParts + 4 * (kMaxCertR + 1));
   w.prog = reinterpret_cast<int*>(take(2 * BH * (size_t)g.nseg + 2));
+  w.dpart = take(g.dustbin ? BH * (size_t)((g.L + 255) / 256) * g.d : 0);
   w.floats = off;
   return w;
 }
