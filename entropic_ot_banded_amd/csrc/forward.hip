@@ -1191,30 +1191,37 @@ __global__ __launch_bounds__(256) void dustbin_step(Geom g, DustArgs p) {
   const double vd_prev = p.first ? 0.0 : p.dstate[4 * bh + 1];
   if (p.v_prev_tail && tid == 0) p.v_prev_tail[bh * L + n] = vd_prev;
   const float* srow = p.sdr + bh * L;
-  // x_j = S_delta,j + v_j (log2) over active j; the corner uses v_delta
+  // x_j = S_delta,j + v_j (log2) over active j; the corner uses v_delta.
+  // One pass: each thread keeps a running maximum m and the sum s of
+  // 2^(x - m) (rescaled when m grows), and the pairs merge in a tree.
   double m = -__builtin_inf();
-  for (int j = tid; j <= n; j += blockDim.x) {
-    const double vj = (j == n) ? vd_prev : (p.v_cur ? p.v_cur[bh * L + j] : 0.0);
-    m = fmax(m, (double)srow[j] + vj);
-  }
-  redd[tid] = m;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) redd[tid] = fmax(redd[tid], redd[tid + s]);
-    __syncthreads();
-  }
-  const double M = redd[0];
   float acc = 0.f;
   for (int j = tid; j <= n; j += blockDim.x) {
     const double vj = (j == n) ? vd_prev : (p.v_cur ? p.v_cur[bh * L + j] : 0.0);
-    acc += exp2_fast((float)((double)srow[j] + vj - M));
+    const double x = (double)srow[j] + vj;
+    if (x > m) {
+      acc = acc * exp2_fast((float)(m - x)) + 1.f;
+      m = x;
+    } else {
+      acc += exp2_fast((float)(x - m));
+    }
   }
+  redd[tid] = m;
   red[tid] = acc;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
+    if (tid < s) {
+      const double m1 = redd[tid], m2 = redd[tid + s];
+      const double mm = fmax(m1, m2);
+      // an empty side (m = -inf) contributes nothing
+      const float a1 = m1 == -__builtin_inf() ? 0.f : red[tid] * exp2_fast((float)(m1 - mm));
+      const float a2 = m2 == -__builtin_inf() ? 0.f : red[tid + s] * exp2_fast((float)(m2 - mm));
+      redd[tid] = mm;
+      red[tid] = a1 + a2;
+    }
     __syncthreads();
   }
+  const double M = redd[0];
   __shared__ double sh_ud;
   __shared__ int sh_exact;
   const float bd = p.b[(size_t)bb * L + n];
