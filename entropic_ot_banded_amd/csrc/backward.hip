@@ -1107,12 +1107,24 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
         const f4 w4 = *reinterpret_cast<const f4*>(wv + cw);
         f4 z4 = {0.f, 0.f, 0.f, 0.f};
         if (MODE == 0) z4 = *reinterpret_cast<const f4*>(vec + cw);
-        // window modifiers of the lane's four entries, one 16-byte read each
-        // (cw is a multiple of 4 and NWC of 16)
-        f4 mv[2 * RM];
+        // dP minus the tail terms, tail step by tail step: the step's two
+        // window modifiers of the lane's four entries come in one 16-byte read
+        // each (cw is a multiple of 4 and NWC of 16) and are used at once
+        f4 br4 = dacc;
+        if (MODE == 1) {
 #pragma unroll
-        for (int k = 0; k < 2 * RM; ++k)
-          if (MODE == 1 && k < 2 * R) mv[k] = *reinterpret_cast<const f4*>(vec + (size_t)k * NWC + cw);
+          for (int k = 0; k < RM; ++k) {
+            if (k < R) {
+              const f4 m0 = *reinterpret_cast<const f4*>(vec + (size_t)(2 * k) * NWC + cw);
+              const f4 m1 = *reinterpret_cast<const f4*>(vec + (size_t)(2 * k + 1) * NWC + cw);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                br4[r] -= COL ? m0[r] * sm0[k] : sm0[k] * m0[r];
+                br4[r] -= COL ? m1[r] * sm1[k] : sm1[k] * m1[r];
+              }
+            }
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int wi = tg * 16 + 4 * lg + r;
@@ -1125,17 +1137,7 @@ __global__ __launch_bounds__(kSwThreads, RM <= 2 ? 4 : 2) void bw_sweep_kernel(G
           } else if (MODE == 2) {
             val[tt][r] = pe;
           } else {
-            float br = dacc[r];
-#pragma unroll
-            for (int k = 0; k < RM; ++k) {
-              if (k < R) {
-                const float m0 = mv[2 * k][r];
-                const float m1 = mv[2 * k + 1][r];
-                br -= COL ? m0 * sm0[k] : sm0[k] * m0;
-                br -= COL ? m1 * sm1[k] : sm1[k] * m1;
-              }
-            }
-            val[tt][r] = pe * br;
+            val[tt][r] = pe * br4[r];
           }
         }
       }
