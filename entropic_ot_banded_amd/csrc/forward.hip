@@ -62,6 +62,33 @@ struct IterArgs {
   int padded_grid;
 };
 
+// One 256-byte row by LDS DMA (a dword per lane): bytes gb + 256 r + 4 lane
+// to lds_row + 4 lane.  The instruction's immediate offset (256 r here) is
+// added to both the global and the LDS address and must be a compile-time
+// constant, hence one case per row r in [0, 16).
+__device__ __forceinline__ void dma_row256(const char* gb, char* lds_row, int r) {
+  char* l = lds_row - 256 * r;
+  switch (r) {
+    case 0: __builtin_amdgcn_global_load_lds(gb, l, 4, 0, 0); break;
+    case 1: __builtin_amdgcn_global_load_lds(gb, l, 4, 256, 0); break;
+    case 2: __builtin_amdgcn_global_load_lds(gb, l, 4, 512, 0); break;
+    case 3: __builtin_amdgcn_global_load_lds(gb, l, 4, 768, 0); break;
+    case 4: __builtin_amdgcn_global_load_lds(gb, l, 4, 1024, 0); break;
+    case 5: __builtin_amdgcn_global_load_lds(gb, l, 4, 1280, 0); break;
+    case 6: __builtin_amdgcn_global_load_lds(gb, l, 4, 1536, 0); break;
+    case 7: __builtin_amdgcn_global_load_lds(gb, l, 4, 1792, 0); break;
+    case 8: __builtin_amdgcn_global_load_lds(gb, l, 4, 2048, 0); break;
+    case 9: __builtin_amdgcn_global_load_lds(gb, l, 4, 2304, 0); break;
+    case 10: __builtin_amdgcn_global_load_lds(gb, l, 4, 2560, 0); break;
+    case 11: __builtin_amdgcn_global_load_lds(gb, l, 4, 2816, 0); break;
+    case 12: __builtin_amdgcn_global_load_lds(gb, l, 4, 3072, 0); break;
+    case 13: __builtin_amdgcn_global_load_lds(gb, l, 4, 3328, 0); break;
+    case 14: __builtin_amdgcn_global_load_lds(gb, l, 4, 3584, 0); break;
+    case 15: __builtin_amdgcn_global_load_lds(gb, l, 4, 3840, 0); break;
+    default: break;
+  }
+}
+
 // floor(a / b) for b > 0 and any sign of a.
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
@@ -598,10 +625,18 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
   int dir = 1;  // sweep direction of the current step (always forward unless PERS)
   auto fold = [&](int kf, int bf, int rbf, bool last, bool fwd, int nthr) {
     const int wc0 = tid - kBlockRows;
-    for (int wc = wc0; wc0 >= 0 && wc0 < nthr && wc < NWC; wc += nthr) {
+    if (wc0 < 0 || wc0 >= nthr) return;
+    float* const pout = s_part_out() + ((size_t)bh * g.nseg + seg) * g.SW - cs;  // indexed by column
+    for (int wc = wc0; wc < NWC; wc += nthr) {
       const int off = wc >> 4;                         // tile offset within block kf's window
       const int c = wrap(rbf + off) * 16 + (wc & 15);  // its ring column
+      // the column's reads are all issued before any is summed (one LDS
+      // round trip per column)
+      float xs[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) xs[w] = colbuf[(bf * kWaves + w) * CBW + (off - w) * 16 + (wc & 15)];
       float s = colsum[c];
+      __builtin_amdgcn_sched_group_barrier(0x100, kWaves + 1, 0);  // the LDS reads first
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         // the tile's index in wave w's strip; the read address stays inside
@@ -609,14 +644,13 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         // in w and unselected values are discarded
         const int lt = off - w;
         const bool wrote = lt >= 0 && lt < NT && kf * kBlockRows + 16 * w < n;
-        const float x = colbuf[(bf * kWaves + w) * CBW + lt * 16 + (wc & 15)];
-        s += wrote ? x : 0.f;
+        s += wrote ? xs[w] : 0.f;
       }
       // columns leave at the low end of the window in a forward sweep, at
       // the high end in a backward one
       if ((fwd ? off < 8 : off >= NWT - 8) || last) {
         const int j = (kf * 8 - g.TL + off) * 16 + (wc & 15);
-        st_shared<PERS>(s_part_out() + ((size_t)bh * g.nseg + seg) * g.SW + (j - cs), s);
+        st_shared<PERS>(pout + j, s);
         // a sweep's last fold leaves its sums in place: the next step's
         // window (this one) takes the segment's own partials from here
         if (!last) s = 0.f;
@@ -721,12 +755,24 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
           // land in another workgroup's LDS).
           if (more) {
             const int slot = wrap(rb + NWT + wave);
+            const int jb = jp0 + wave * 16;
+            if (jb >= 0 && jb + 15 < n) {
+              // all 16 rows real: one lane address for the tile, the row in
+              // the immediate offset (no per-row address arithmetic)
+              const char* gb = Kb + (uint32_t)(jb * RB + lane * 4);
 #pragma unroll
-            for (int i = 0; i < 16 / NEWLD; ++i) {
-              const int r = (16 / NEWLD) * part + i;
-              int j = jp0 + wave * 16 + r;
-              j = j < 0 ? 0 : (j >= n ? n - 1 : j);
-              __builtin_amdgcn_global_load_lds(Kb + (uint32_t)(j * RB + lane * 4), kw + (slot * 16 + r) * RS, 4, 0, 0);
+              for (int i = 0; i < 16 / NEWLD; ++i) {
+                const int r = (16 / NEWLD) * part + i;
+                dma_row256(gb, kw + (slot * 16 + r) * RS, r);
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < 16 / NEWLD; ++i) {
+                const int r = (16 / NEWLD) * part + i;
+                int j = jb + r;
+                j = j < 0 ? 0 : (j >= n ? n - 1 : j);
+                __builtin_amdgcn_global_load_lds(Kb + (uint32_t)(j * RB + lane * 4), kw + (slot * 16 + r) * RS, 4, 0, 0);
+              }
             }
           }
         } else {
@@ -891,7 +937,11 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         consume(NT - 1, accP, wP);
 #pragma unroll
         for (int q = NT; q < NPF; ++q) prefetch(q);
-        bool bad = false;
+        // every row sum in [2^-120, 2^120] (and not NaN): its bits minus
+        // those of 2^-120, as unsigned, stay at most the span's (rows past
+        // the sequence count as 1)
+        constexpr uint32_t kLoBits = 0x03800000u, kSpan = 0x7b800000u - 0x03800000u;
+        uint32_t worst = 0u;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           rs[r] = row16_sum(rs[r]);
@@ -899,9 +949,12 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
             ed[r] = exp2_fast(xd[r]);
             rs[r] += ed[r];
           }
-          if (rowok[r]) bad |= !(rs[r] >= 0x1p-120f && rs[r] <= 0x1p120f);
+          float x = rs[r];
+          if (partial) x = rowok[r] ? x : 1.f;
+          const uint32_t d = __float_as_uint(x) - kLoBits;
+          worst = worst > d ? worst : d;
         }
-        need_safe = __any(bad);
+        need_safe = __any(worst > kSpan);
       } else {
 #pragma unroll
         for (int q = 0; q < NPF; ++q) prefetch(q);
@@ -967,13 +1020,13 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
         float rsv = rs[0], av = ar[0], shv = shift[0];
         bool okv = rowok[0];
 #pragma unroll
-        for (int r = 1; r < 4; ++r)
-          if (rsel == r) {
-            rsv = rs[r];
-            av = ar[r];
-            shv = shift[r];
-            okv = rowok[r];
-          }
+        for (int r = 1; r < 4; ++r) {
+          const bool pick = rsel == r;
+          rsv = pick ? rs[r] : rsv;
+          av = pick ? ar[r] : av;
+          shv = pick ? shift[r] : shv;
+          okv = pick ? rowok[r] : okv;
+        }
         if (lr < 4 && okv) {
           const int i = i0 + 4 * lg + rsel;
           const double u = log2_split(av * __builtin_amdgcn_rcpf(rsv)) - (double)shv - vref;
