@@ -394,7 +394,7 @@ constexpr int kStallTestBias = 1 << 30;
 // least the band's 16 (TL + TR) columns (then the windows of segments two
 // apart are disjoint); the host launches this instance only then.  All
 // workgroups must be resident (cooperative launch).
-template <typename T, int D, int NT, bool PERS>
+template <typename T, int D, int NT, bool PERS, bool FE = false>
 __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan q) {
   constexpr int RB = D * Elt<T>::kBytes;  // bytes per Q/K row
   constexpr int NCH = RB / 64;             // 16-byte lane chunks per row
@@ -890,51 +890,78 @@ __global__ __launch_bounds__(512) void iter_kernel(Geom g, IterArgs p0, StepPlan
       // there as well.
       bool need_safe = s_first() != 0;
       if (!need_safe) {
-        // fast path: shift vref only; pipelined MFMA / exp
-        auto consume = [&](int t, const f4& acc, float w) {
-          float x[4];
+        // fast path: shift vref only; pipelined MFMA / exp.  FE instance (the
+        // host launches it when the band's only edge-crossing strip tiles
+        // are the first and last): those two take the additive band masks
+        // and no tile has a branch, so each tile's work is one scheduling
+        // region; rows past the sequence are not masked in the loop, their
+        // entries are zeroed after it (every real row's arithmetic is the
+        // other instance's; both loops in one instance exhaust the registers)
+        auto tile_loop = [&](auto fec) {
+          constexpr bool kFE = decltype(fec)::value;
+          auto consume = [&](int t, const f4& acc, float w) {
+            float x[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(acc[r], g.scale2, w);
-          if ((emask >> t) & 1u) mask_tile(t, x);
+            for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(acc[r], g.scale2, w);
+            if constexpr (kFE) {
+              if (t == 0 || t == NT - 1) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e[t][r] = exp2_fast(x[r]);
-            rs[r] += e[t][r];
+                for (int r = 0; r < 4; ++r) x[r] += t == 0 ? mb0[r] : mb1[r];
+              }
+            } else {
+              if ((emask >> t) & 1u) mask_tile(t, x);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              e[t][r] = exp2_fast(x[r]);
+              rs[r] += e[t][r];
+            }
+            // pin the sums here: otherwise the exps sink below the tile loop
+            asm volatile("" : "+v"(rs[0]), "+v"(rs[1]), "+v"(rs[2]), "+v"(rs[3]));
+          };
+          u4 kbA[NCH], kbB[NCH];
+          float wA, wB;
+          read_tile(0, kbA, wA);
+          f4 accP = {0.f, 0.f, 0.f, 0.f};
+          float wP = 0.f;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t < NPF) {
+              asm volatile("" ::: "memory");  // keep slice t at tile t (no hoisting)
+              prefetch(t);
+            }
+            if (t & 1) {
+              if (t + 1 < NT) read_tile(t + 1, kbA, wA);
+              const f4 acc = mma_tile(kbB);
+              if (t > 0) consume(t - 1, accP, wP);
+              accP = acc;
+              wP = wB;
+            } else {
+              if (t + 1 < NT) read_tile(t + 1, kbB, wB);
+              const f4 acc = mma_tile(kbA);
+              if (t > 0) consume(t - 1, accP, wP);
+              accP = acc;
+              wP = wA;
+            }
+            // tile t-1's exp/sum work stays in this iteration, interleaved with
+            // tile t's MFMAs and tile t+1's LDS reads (with every exp after the
+            // loop, the LDS/MFMA and VALU phases of all waves run one after
+            // the other)
+            __builtin_amdgcn_sched_barrier(0);
           }
-          // pin the sums here: otherwise the exps sink below the tile loop
-          asm volatile("" : "+v"(rs[0]), "+v"(rs[1]), "+v"(rs[2]), "+v"(rs[3]));
+          consume(NT - 1, accP, wP);
         };
-        u4 kbA[NCH], kbB[NCH];
-        float wA, wB;
-        read_tile(0, kbA, wA);
-        f4 accP = {0.f, 0.f, 0.f, 0.f};
-        float wP = 0.f;
+        if constexpr (FE) {
+          tile_loop(std::true_type{});
+          if (partial) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t < NPF) {
-            asm volatile("" ::: "memory");  // keep slice t at tile t (no hoisting)
-            prefetch(t);
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) e[tt][r] = rowok[r] ? e[tt][r] : 0.f;
           }
-          if (t & 1) {
-            if (t + 1 < NT) read_tile(t + 1, kbA, wA);
-            const f4 acc = mma_tile(kbB);
-            if (t > 0) consume(t - 1, accP, wP);
-            accP = acc;
-            wP = wB;
-          } else {
-            if (t + 1 < NT) read_tile(t + 1, kbB, wB);
-            const f4 acc = mma_tile(kbA);
-            if (t > 0) consume(t - 1, accP, wP);
-            accP = acc;
-            wP = wA;
-          }
-          // tile t-1's exp/sum work stays in this iteration, interleaved with
-          // tile t's MFMAs and tile t+1's LDS reads (with every exp after the
-          // loop, the LDS/MFMA and VALU phases of all waves run one after
-          // the other)
-          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          tile_loop(std::false_type{});
         }
-        consume(NT - 1, accP, wP);
 #pragma unroll
         for (int q = NT; q < NPF; ++q) prefetch(q);
         // every row sum in [2^-120, 2^120] (and not NaN): its bits minus
@@ -2016,19 +2043,19 @@ static hipError_t forward_impl(const Geom& g, const FwdLaunch& f, const Workspac
   // compile-time tile count: the smallest instance covering the band
   const void* ik;
   const void* ikp;  // persistent instance
-  if (g.NT <= 3) {
-    ik = reinterpret_cast<const void*>(iter_kernel<T, D, 3, false>);
-    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, 3, true>);
-  } else if (g.NT <= 5) {
-    ik = reinterpret_cast<const void*>(iter_kernel<T, D, 5, false>);
-    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, 5, true>);
-  } else if (g.NT <= 9) {
-    ik = reinterpret_cast<const void*>(iter_kernel<T, D, 9, false>);
-    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, 9, true>);
-  } else {
-    ik = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles, false>);
-    ikp = reinterpret_cast<const void*>(iter_kernel<T, D, kMaxTiles, true>);
-  }
+  // a band whose only edge-crossing strip tiles are the first and last takes
+  // the persistent instance compiled for that case (FE)
+  const bool ends_only = (g.edge_mask & ~(1u | (1u << (g.NT - 1)))) == 0u;
+  auto pick = [&](auto ntc) {
+    constexpr int N = decltype(ntc)::value;
+    ik = reinterpret_cast<const void*>(iter_kernel<T, D, N, false>);
+    ikp = ends_only ? reinterpret_cast<const void*>(iter_kernel<T, D, N, true, true>)
+                    : reinterpret_cast<const void*>(iter_kernel<T, D, N, true, false>);
+  };
+  if (g.NT <= 3) pick(std::integral_constant<int, 3>{});
+  else if (g.NT <= 5) pick(std::integral_constant<int, 5>{});
+  else if (g.NT <= 9) pick(std::integral_constant<int, 9>{});
+  else pick(std::integral_constant<int, kMaxTiles>{});
   err = ensure_lds(ik, iter_lds);
   if (err != hipSuccess) return err;
   err = ensure_lds(ikp, iter_lds);
