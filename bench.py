@@ -147,7 +147,7 @@ def load_pmc(launch_units=None):
 PROF_ARGS = ("--no-cpu-baseline --converge-tol 0 --certificate-rmax 0 --contraction-block 0 --no-peaks "
              "--r4-steps 0 --no-other-configs")
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d $OUT/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 2 "
+             "-d $OUT/trace -o run -- python3 $REPO/bench.py --steps 5 --warmup 20 "
              + PROF_ARGS)
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
                "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS GRBM_GUI_ACTIVE")
@@ -204,6 +204,15 @@ def summarize(d):
                   f"{float(it[0]['AverageNs']) / 1e3:.2f} us per dispatch = "
                   f"{float(it[0]['AverageNs']) / 1e3 / spd:.2f} us per step "
                   f"(min {float(it[0]['MinNs']) / 1e3 / spd:.2f}, max {float(it[0]['MaxNs']) / 1e3 / spd:.2f})"]
+        # the timed dispatches (the last 5 of the main workload: warm-up first)
+        tr = glob.glob(os.path.join(d, "trace", "*kernel_trace.csv"))
+        if tr:
+            disp = [r for r in _csv_rows(tr[0]) if "iter_kernel" in r["Kernel_Name"]]
+            disp.sort(key=lambda r: int(r["Start_Timestamp"]))
+            us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 / spd for r in disp[-5:]]
+            if us:
+                lines.append(f"timed dispatches (the last {len(us)}): " + ", ".join(f"{x:.2f}" for x in us)
+                             + f" us per step, average {sum(us) / len(us):.2f}")
     logf = os.path.join(d, "trace.log")
     if os.path.exists(logf):
         for ln in open(logf):
@@ -480,8 +489,11 @@ def time_workload(eoba, torch, prob, steps, warmup, dev, tensors=None):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 20 untimed steps first: the step time falls by about 2% over the first
+    # ten or so steps of a process (the clocks settling under load), and the
+    # line reports the steady state
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--R", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA/exp peak probes")
