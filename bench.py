@@ -168,6 +168,10 @@ EXIT_NOTE = ("  (exit status 0, or 139 from the profiler's teardown after a coop
 TCC_COUNTERS = "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum"
 TCC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + TCC_COUNTERS + " --output-format csv "
            "-d $OUT/tcc -o run -- python3 $REPO/bench.py --steps 2 --warmup 1 " + PROF_ARGS)
+LDS_STRIDES = (256, 272, 288, 304, 320)
+LDS_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS "
+           "--output-format csv -d $OUT/lds -o run -- python3 $REPO/bench.py --lds-probe > $OUT/lds_probe.json")
+LDS_FILE = os.path.join(ROOT, "profiles", "lds_read_patterns.txt")
 SWEEP_FILE = os.path.join(ROOT, "profiles", "sweep_kernels_long_context.txt")
 L2_FILE = os.path.join(ROOT, "profiles", "l2_dram_long_context.txt")
 
@@ -188,7 +192,11 @@ def summarize(d):
     """Write the profile summaries kept under profiles/ from rocprofv3 CSV
     output in d/trace (kernel trace + stats), d/fetch and d/write (PMC)."""
     import glob
-    stats = _csv_rows(glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))[0])
+    traces = glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))
+    if not traces:  # an LDS probe run only
+        summarize_lds(d)
+        return
+    stats = _csv_rows(traces[0])
     stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["Kernel statistics of the long-context workload (B=1, H=8, L=32768, d=128, W=256,",
              "T=100, R=2, bf16 inputs): 5 timed + 2 warm-up forward+backward steps.",
@@ -259,6 +267,7 @@ def summarize(d):
     summarize_sq(d)
     summarize_sweeps(d)
     summarize_l2(d)
+    summarize_lds(d)
 
 
 def _per_kernel(path, names):
@@ -304,7 +313,11 @@ def summarize_sweeps(d):
     (FETCH_SIZE, WRITE_SIZE, copy-calibrated) and the fraction of the HBM
     floor their time reaches."""
     import glob
-    stats = _csv_rows(glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))[0])
+    traces = glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))
+    if not traces:  # an LDS probe run only
+        summarize_lds(d)
+        return
+    stats = _csv_rows(traces[0])
     try:
         with open(PMC_FILE) as f:
             pmc = json.load(f)
@@ -362,6 +375,67 @@ def summarize_l2(d):
               "  (millions per dispatch); dram_frac = TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ.",
               f"  kernel sources hash {kernel_source_hash()}"]
     with open(L2_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def lds_probe():
+    """Cycles per wave-wide 128-bit LDS read per CU for the step kernel's
+    K-tile read pattern at each ring row stride (sinkattn_measure_lds)."""
+    import torch
+
+    import entropic_ot_banded_amd as eoba
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    eoba.load_library()
+    out = {str(rs): round(eoba.measure_lds(rs, device="cuda:0"), 3) for rs in LDS_STRIDES}
+    out["256_xor"] = round(eoba.measure_lds(256, swizzle=True, device="cuda:0"), 3)
+    print(json.dumps({"lds_probe": {"cycles_per_read": out, "read_bytes": 1024,
+                                    "pattern": "lane (r, g): 16 bytes at 16 g + 64 c of row r, c = 0..3; "
+                                               "8 waves x 17 tiles of a 32-tile ring"}}))
+
+
+def summarize_lds(d):
+    """Bank-conflict cycles per LDS instruction of each LDS probe variant
+    (one rocprofv3 --pmc pass) beside the cycles per read the same run
+    measured."""
+    per = {}
+    path = os.path.join(d, "lds")
+    if not os.path.isdir(path):
+        return
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        return
+    for r in _csv_rows(files[0]):
+        if "lds_probe_kernel" not in r["Kernel_Name"]:
+            continue
+        key = r["Kernel_Name"].split("lds_probe_kernel<")[1].split(">")[0]
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cyc = {}
+    jf = os.path.join(d, "lds_probe.json")
+    if os.path.exists(jf):
+        with open(jf) as f:
+            for line in f:
+                if line.startswith("{"):
+                    cyc = json.loads(line)["lds_probe"]["cycles_per_read"]
+    lines = ["LDS read pattern of the fused step kernel's K-tile operand reads (sinkattn_measure_lds):",
+             "one workgroup of 8 waves per CU, each wave reading 17 consecutive tiles of a 32-tile",
+             "ring of 16-row tiles per pass; lane (r, g) reads the 16 bytes at 16 g + 64 c of row r",
+             "(c = 0..3), one wave-wide 128-bit read = 1024 bytes.", "", HOW, "  " + LDS_CMD,
+             "  " + SUMMARIZE_CMD, "",
+             f"{'row bytes':>10} {'swizzle':>8} {'cycles/read':>12} {'B/clk/CU':>9} {'conflict cyc/LDS inst':>22}"]
+    for key in sorted(per, key=lambda k: (int(k.split(",")[0]), k)):
+        rs, swz = key.split(",")[0].strip(), "true" in key
+        v = per[key]
+        conf = sum(v.get("SQ_LDS_BANK_CONFLICT", [0.0])) / max(sum(v.get("SQ_INSTS_LDS", [1.0])), 1.0)
+        c = cyc.get(rs + ("_xor" if swz else ""))
+        lines.append(f"{rs:>10} {('xor' if swz else '-'):>8} {c if c is not None else float('nan'):12.2f} "
+                     f"{(1024.0 / c) if c else float('nan'):9.1f} {conf:22.2f}")
+    lines += ["", "  conflict cyc/LDS inst = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS over the probe's dispatches",
+              "  (the ring fill's writes included, under 1% of its LDS instructions); the step kernel",
+              "  keeps 272-byte rows (288 would fit only by moving its column partials into the row padding)."]
+    with open(LDS_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -514,9 +588,14 @@ def main():
                     help="also time the same workload with the R=4 tail over this many steps (0: skip)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the step times of the tiny, mid, protein-like and dustbin workloads")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only measure the LDS read pattern of the step kernel at each ring row stride")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.lds_probe:
+        lds_probe()
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

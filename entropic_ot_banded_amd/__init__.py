@@ -7,9 +7,9 @@ autograd wrapper; torch supplies device memory and streams only.
 
 from .binding import (  # noqa: F401
     EXPORTED, SINKATTN_BF16, SINKATTN_F32, Shape, SinkattnError, backward, block_contraction, forward,
-    forward_converge, forward_noalloc, load_library, measure_peaks, status_string, tail_certificate, tail_offset,
+    forward_converge, forward_noalloc, load_library, measure_lds, measure_peaks, status_string, tail_certificate, tail_offset,
     tail_stack, timing_collect, timing_enable, workspace_bytes,
 )
 from .autograd import sinkhorn_attention  # noqa: F401
 
-__version__ = "1.0.0"
+__version__ = "1.1.0"

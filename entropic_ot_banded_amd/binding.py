@@ -32,7 +32,7 @@ EXPORTED = ("sinkattn_workspace_bytes", "sinkattn_tail_offset", "sinkattn_forwar
             "sinkattn_forward_noalloc", "sinkattn_forward_converge", "sinkattn_backward", "sinkattn_tail_certificate",
             "sinkattn_block_contraction", "sinkattn_timing_enable", "sinkattn_timing_collect",
             "sinkattn_status_string", "sinkattn_last_hip_error", "sinkattn_version",
-            "sinkattn_measure_peaks")
+            "sinkattn_measure_peaks", "sinkattn_measure_lds")
 
 
 class SinkattnError(RuntimeError):
@@ -97,6 +97,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     dp = ctypes.POINTER(ctypes.c_double)
     lib.sinkattn_measure_peaks.argtypes = [dp, dp, dp, vp]
     lib.sinkattn_measure_peaks.restype = i32
+    lib.sinkattn_measure_lds.argtypes = [i32, i32, dp, vp]
+    lib.sinkattn_measure_lds.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -374,6 +376,20 @@ def measure_peaks(device=None) -> dict:
                                                    _stream(dev))
     _check(st)
     return {"mfma_bf16_flops": mfma.value, "exp_per_s": ex.value, "clock_hz": clk.value}
+
+
+def measure_lds(row_stride: int, swizzle: bool = False, device=None) -> float:
+    """Shader cycles per wave-wide 128-bit LDS read per CU for the step
+    kernel's K-tile read pattern with the given row stride (see
+    sinkattn_measure_lds); blocks for a few ms."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    cyc = ctypes.c_double()
+    with torch.cuda.device(dev):
+        st = load_library().sinkattn_measure_lds(int(row_stride), 1 if swizzle else 0, ctypes.byref(cyc),
+                                                 _stream(dev))
+    _check(st)
+    return cyc.value
 
 
 def tail_stack(workspace, Q, R: int, lengths=None, dustbin=False):

@@ -25,6 +25,7 @@ hipError_t launch_block_diameters(const Geom& g, int dtype, const void* Q, const
 hipError_t launch_certificate(const Geom& g, int dtype, const BwdLaunch& base, int R_max, const Workspace& w,
                               float* dQs, float* dKs, double* eta, hipStream_t st);
 hipError_t launch_peak_probes(double* mfma_flops, double* exps, double* clock_hz, hipStream_t st);
+hipError_t launch_lds_probe(int row_stride, int swizzle, double* cycles_per_read, hipStream_t st);
 
 namespace {
 
@@ -240,7 +241,7 @@ extern "C" {
 
 const char* sinkattn_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
-int sinkattn_version(void) { return 10000; }
+int sinkattn_version(void) { return 10100; }  // 1.1.0: sinkattn_measure_lds
 
 const char* sinkattn_status_string(int status) {
   switch (status) {
@@ -427,6 +428,14 @@ int sinkattn_block_contraction(const void* Q, const void* K, int W, const sinkat
 int sinkattn_measure_peaks(double* mfma_bf16_flops, double* exp_per_s, double* clock_hz, hipStream_t stream) {
   if (!mfma_bf16_flops || !exp_per_s) return SINKATTN_EINVAL;
   return hip_status(launch_peak_probes(mfma_bf16_flops, exp_per_s, clock_hz, stream));
+}
+
+int sinkattn_measure_lds(int row_stride, int swizzle, double* cycles_per_read, hipStream_t stream) {
+  if (!cycles_per_read) return SINKATTN_EINVAL;
+  const bool ok = swizzle ? (swizzle == 1 && row_stride == 256)
+                          : (row_stride >= 256 && row_stride <= 320 && row_stride % 16 == 0);
+  if (!ok) return SINKATTN_EINVAL;
+  return hip_status(launch_lds_probe(row_stride, swizzle, cycles_per_read, stream));
 }
 
 }  // extern "C"

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
+#include "geom.hpp"
 
 namespace sinkattn {
 
@@ -34,6 +35,8 @@ constexpr int kExpChains = 16;
 constexpr int kMfmaChains = 2;
 constexpr int kExpIters = 16384;
 constexpr int kMfmaIters = 65536;
+constexpr int kLdsProbeGroups = 256;  // one workgroup per CU (the ring fills most of the LDS)
+constexpr int kLdsProbeIters = 200;
 
 __device__ __forceinline__ void clock_mark(int which) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -80,6 +83,71 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, fl
   clock_mark(1);
 }
 
+// LDS read pattern of the fused step kernel's K-tile operand reads: eight
+// waves of one workgroup per CU each read, tile after tile, 17 consecutive
+// tiles of a 32-tile ring of 16-row tiles (row stride RS bytes), lane (r, g)
+// of a read taking the 16 bytes at 16 g + 64 c of row r (c = 0..3, one
+// 128-bit read per c).  SWZ: 256-byte rows whose 16-byte chunk p sits at
+// position p ^ ((r ^ 2 r) & 15) (each lane then forms four chunk offsets).
+// Every workgroup records the shader cycles of its read loop.
+__device__ unsigned long long g_lds_cycles[kLdsProbeGroups];
+
+template <int RS, bool SWZ>
+__global__ __launch_bounds__(512) void lds_probe_kernel(int iters, unsigned sentinel) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int TILEB = 16 * RS;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = tid >> 6;
+  for (int i = tid; i < 32 * TILEB / 4; i += 512) reinterpret_cast<uint32_t*>(smem)[i] = i * 2654435761u;
+  __syncthreads();
+  int offc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int pos = lg + 4 * c;
+    if (SWZ) pos ^= (lr ^ (2 * lr)) & 15;
+    offc[c] = lr * RS + pos * 16;  // < 16 RS: inside the tile
+  }
+  u4 acc = {0u, 0u, 0u, 0u};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int t = 0; t < 17; ++t) {
+      const char* base = smem + ((wave + t + it) & 31) * TILEB;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc ^= ld16(base + offc[c]);
+    }
+  }
+  const unsigned h = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  __syncthreads();
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (h == sentinel) g_probe_sink[tid & 255] = 1.f;
+  if (tid == 0) g_lds_cycles[blockIdx.x] = t1 - t0;
+}
+
+template <int RS, bool SWZ>
+hipError_t time_lds_probe(hipStream_t st, double* cycles_per_read) {
+  const size_t lds = (size_t)32 * 16 * RS;
+  hipError_t e = ensure_lds(reinterpret_cast<const void*>(lds_probe_kernel<RS, SWZ>), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((lds_probe_kernel<RS, SWZ>), dim3(kLdsProbeGroups), dim3(512), lds, st, kLdsProbeIters / 8, 0u);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL((lds_probe_kernel<RS, SWZ>), dim3(kLdsProbeGroups), dim3(512), lds, st, kLdsProbeIters, 0u);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  unsigned long long cyc[kLdsProbeGroups];
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(cyc, HIP_SYMBOL(g_lds_cycles), sizeof(cyc), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  double sum = 0.0;
+  for (int i = 0; i < kLdsProbeGroups; ++i) sum += (double)cyc[i];
+  // wave-wide 128-bit reads per workgroup (the CU's LDS serves all of them)
+  const double reads = (double)kLdsProbeIters * 17 * 4 * 8;
+  *cycles_per_read = sum / kLdsProbeGroups / reads;
+  return hipSuccess;
+}
+
 // One timed launch (after an untimed short one that brings the clocks up):
 // elapsed seconds and the shader clock over workgroup 0's span.
 template <typename Kernel>
@@ -116,6 +184,18 @@ hipError_t time_probe(Kernel kernel, int iters, hipStream_t st, double* seconds,
 }
 
 }  // namespace
+
+hipError_t launch_lds_probe(int row_stride, int swizzle, double* cycles_per_read, hipStream_t st) {
+  if (swizzle) return row_stride == 256 ? time_lds_probe<256, true>(st, cycles_per_read) : hipErrorInvalidValue;
+  switch (row_stride) {
+    case 256: return time_lds_probe<256, false>(st, cycles_per_read);
+    case 272: return time_lds_probe<272, false>(st, cycles_per_read);
+    case 288: return time_lds_probe<288, false>(st, cycles_per_read);
+    case 304: return time_lds_probe<304, false>(st, cycles_per_read);
+    case 320: return time_lds_probe<320, false>(st, cycles_per_read);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_peak_probes(double* mfma_flops, double* exps, double* clock_hz, hipStream_t st) {
   double t_exp = 0.0, t_mfma = 0.0, clk_exp = 0.0, clk_mfma = 0.0;

@@ -285,6 +285,23 @@ int sinkattn_timing_collect(double *total_ms, long long *steps);
 int sinkattn_measure_peaks(double *mfma_bf16_flops, double *exp_per_s, double *clock_hz,
                            hipStream_t stream);
 
+/* LDS service rate for the operand read pattern of the fused step kernel's
+ * K tiles (a measurement behind its layout; no part of the method).  One
+ * workgroup of eight waves per CU reads a ring of 32 tiles of 16 rows, each
+ * wave 17 consecutive tiles per pass, lane (r, g) of a 128-bit read taking
+ * the 16 bytes at 16 g + 64 c of row r (c = 0..3); rows are `row_stride`
+ * bytes apart (256, 272, 288, 304 or 320), and with `swizzle` = 1 (only for
+ * 256-byte rows) chunk p of row r is stored at chunk position
+ * p ^ ((r ^ 2 r) & 15).  Runs an untimed short launch and a timed one on
+ * `stream` and waits for them (blocking):
+ *   cycles_per_read : out, shader cycles per wave-wide 128-bit read per CU
+ *                     (1024 bytes; 4 when the LDS serves 256 bytes per clock
+ *                     without bank conflicts).
+ * Allocates no device memory.  Returns SINKATTN_EINVAL on a NULL output or
+ * an unsupported stride / swizzle pair, SINKATTN_EHIP on a launch or copy
+ * failure. */
+int sinkattn_measure_lds(int row_stride, int swizzle, double *cycles_per_read, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char *sinkattn_status_string(int status);
 

@@ -141,6 +141,12 @@ int main() {
   for (int code = -7; code <= 0; ++code) EXPECT(std::strcmp(sinkattn_status_string(code), "unknown status") != 0);
   EXPECT(std::strcmp(sinkattn_status_string(99), "unknown status") == 0);
   EXPECT(sinkattn_measure_peaks(nullptr, nullptr, nullptr, nullptr) == SINKATTN_EINVAL);
+  double cyc = 0.0;
+  EXPECT(sinkattn_measure_lds(288, 0, nullptr, nullptr) == SINKATTN_EINVAL);
+  EXPECT(sinkattn_measure_lds(280, 0, &cyc, nullptr) == SINKATTN_EINVAL);
+  EXPECT(sinkattn_measure_lds(336, 0, &cyc, nullptr) == SINKATTN_EINVAL);
+  EXPECT(sinkattn_measure_lds(272, 1, &cyc, nullptr) == SINKATTN_EINVAL);
+  EXPECT(sinkattn_measure_lds(256, 2, &cyc, nullptr) == SINKATTN_EINVAL);
   EXPECT(sinkattn_version() >= 10000);
 
   EXPECT(g_stub_calls == 0);

@@ -30,4 +30,8 @@ hipError_t launch_peak_probes(double*, double*, double*, hipStream_t) {
   ++g_stub_calls;
   return hipErrorInvalidValue;
 }
+hipError_t launch_lds_probe(int, int, double*, hipStream_t) {
+  ++g_stub_calls;
+  return hipErrorInvalidValue;
+}
 }  // namespace sinkattn

@@ -222,3 +222,10 @@ def test_forward_noalloc_validation_before_launch(lib):
     assert call(big, W=256) == binding.SINKATTN_ESCRATCH
     long_ctx = _shape(B=1, H=8, L=32768, d=128, dtype=binding.SINKATTN_BF16)
     assert eoba.workspace_bytes(long_ctx, 256, 4) <= binding.NOALLOC_SCRATCH_BYTES
+
+
+def test_measure_lds_validation(lib):
+    c = ctypes.c_double()
+    assert lib.sinkattn_measure_lds(288, 0, None, None) == binding.SINKATTN_EINVAL
+    for stride, swizzle in ((280, 0), (336, 0), (240, 0), (272, 1), (256, 2)):
+        assert lib.sinkattn_measure_lds(stride, swizzle, ctypes.byref(c), None) == binding.SINKATTN_EINVAL

@@ -17,3 +17,19 @@ def test_measure_peaks_plausible():
     assert 0.2 * 2.5e15 < p["mfma_bf16_flops"] < 1.05 * 2.5e15, p
     assert 0.2 * 256 * 2.4e9 * 16 < p["exp_per_s"] < 1.05 * 256 * 2.4e9 * 64, p
     assert p["clock_hz"] == 0.0 or 0.5e9 < p["clock_hz"] < 2.6e9, p
+
+
+def test_measure_lds_read_patterns():
+    """The step kernel's K-tile read pattern at several row strides: no
+    stride gets more than 256 bytes per clock per CU out of the LDS (at least
+    4 cycles per 1 KB wave read), unpadded 256-byte rows conflict heavily,
+    and 288-byte rows read faster than the 272-byte ones the kernel uses."""
+    print("case: sinkattn_measure_lds on cuda:0", flush=True)
+    c = {s: eoba.measure_lds(s, device="cuda:0") for s in (256, 272, 288, 304, 320)}
+    cx = eoba.measure_lds(256, swizzle=True, device="cuda:0")
+    print("cycles per wave-wide 128-bit read:", c, "xor-swizzled 256:", cx, flush=True)
+    for v in list(c.values()) + [cx]:
+        assert 3.5 < v < 64.0, (c, cx)
+    assert c[256] > 2.0 * c[272], c
+    assert c[288] < 0.85 * c[272], c
+    assert cx < 0.5 * c[256], (c, cx)
